@@ -1,0 +1,198 @@
+/*
+ * pa.h -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpa.so: a slot-mapped store of new keys/values into a cache made
+ * of fixed-size blocks, paged decode attention (one query token per sequence)
+ * and causal varlen prefill attention over the same paged cache.
+ *
+ * What the operations compute (no code is taken from these sources):
+ *   - nano-vllm hub page (pomoai.com), section "Attention + Triton Kernel":
+ *     keys/values computed for new tokens are written into preallocated cache
+ *     blocks through a per-token slot mapping;
+ *   - same page, section "KV Cache block management": blocks hold a fixed
+ *     256 tokens;
+ *   - CSDN essay comparing nanoVLLM and vLLM, first section (KV-cache
+ *     management): a per-sequence block table maps logical blocks to physical
+ *     blocks that need not be contiguous; a new block is taken when a sequence
+ *     reaches 256k+1 tokens, so a sequence of n tokens owns ceil(n/256) blocks;
+ *   - same essay, third section (attention computation): the attention is the
+ *     exact softmax(scale * q K^T) V, computed in tiles kept on chip;
+ *   - same essay, reading vLLM's attention module: prefill (many tokens per
+ *     sequence, compute-bound) and decode (one token per sequence, bound by
+ *     reading the cache) are separate kernels.
+ *
+ * Conventions shared by every entry point
+ *   bf16        : IEEE bfloat16, passed as raw 16-bit patterns.
+ *   D           : head_dim; only 128 is supported.
+ *   block_size  : tokens per cache block; only 256 is supported.
+ *   Hkv, Hq     : key/value heads and query heads; G = Hq / Hkv must be
+ *                 1, 2, 4 or 8 and query head h reads kv head h / G
+ *                 (contiguous grouped-query heads).
+ *   slot        : a cache position; slot s is row (s % block_size) of physical
+ *                 block (s / block_size).
+ *   K cache     : bf16 [num_blocks][Hkv][D/8][block_size][8]; element (slot s,
+ *                 kv head g, dim d) sits at
+ *                 ((((s/bs)*Hkv + g)*(D/8) + d/8)*bs + s%bs)*8 + d%8.
+ *                 Each 16-byte chunk holds 8 consecutive dims of one token, and
+ *                 one block-head is one contiguous 64 KiB tile.
+ *   V cache     : bf16 [num_blocks][Hkv][block_size][D]; element (s, g, d) sits
+ *                 at (((s/bs)*Hkv + g)*bs + s%bs)*D + d.
+ *   block_table : int32 [batch][max_blocks_per_seq], row-major; entry
+ *                 [b][j] is the physical block of tokens j*bs .. j*bs+bs-1 of
+ *                 sequence b.  Only the first ceil(context_lens[b]/bs) entries
+ *                 of a row are read.
+ *
+ * Memory and streams
+ *   Every array argument is a DEVICE pointer owned by the caller (except the
+ *   host array of pa_validate_slots).  The library allocates nothing, keeps no
+ *   state beyond cached device attributes, and is thread-safe.  Every call is
+ *   asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
+ *   stream) on the current device.  The caller orders a store before the
+ *   attention that reads it by issuing both on one stream.
+ *
+ * Errors
+ *   Entry points return PA_OK or a negative PA_ERR_* code.  All argument checks
+ *   run on the host before anything is launched; on an error nothing is
+ *   launched and pa_last_error_detail() describes it (thread-local).  An empty
+ *   batch (num_tokens == 0, batch == 0) is a successful no-op.  No C++
+ *   exception crosses the ABI.
+ *
+ * Data preconditions (not checked on the host; device code never reads or
+ * writes outside the arrays whatever the data, but the affected outputs are
+ * then unspecified):
+ *   - slots are < num_blocks*block_size (a negative slot means "skip");
+ *   - no two tokens of one pa_store_kv call share a slot;
+ *   - block_table entries that are read lie in [0, num_blocks);
+ *   - 0 <= context_lens[b] <= max_blocks_per_seq*block_size;
+ *   - for prefill, 0 <= q_len_b <= context_lens[b].
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 256
+#define PA_HEAD_DIM 128
+#define PA_K_CHUNK 8
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_PTR = -1,      /* a required pointer is NULL */
+  PA_ERR_BAD_SHAPE = -2,     /* negative sizes, Hq % Hkv != 0, ... */
+  PA_ERR_UNSUPPORTED = -3,   /* head_dim != 128, block_size != 256, G not 1/2/4/8 */
+  PA_ERR_ALIGN = -4,         /* a bf16 array is not 16-byte aligned */
+  PA_ERR_WORKSPACE = -5,     /* workspace missing or too small */
+  PA_ERR_HIP = -6,           /* the HIP runtime reported an error */
+  PA_ERR_SLOT_RANGE = -7,    /* pa_validate_slots: a slot >= num_slots */
+  PA_ERR_DUPLICATE_SLOT = -8 /* pa_validate_slots: two tokens share a slot */
+};
+
+/*
+ * pa_store_kv -- write each new token's keys and values into its cache slot.
+ *
+ * For every i < num_tokens with slot_mapping[i] >= 0, copies the bits of
+ * k_new[i][g][0..D) into the K cache and v_new[i][g][0..D) into the V cache at
+ * slot slot_mapping[i], for every kv head g.  Tokens whose slot is negative
+ * are skipped.  A bit copy: the cache afterwards holds exactly the input bits.
+ *
+ *   k_new, v_new  : bf16 [num_tokens][num_kv_heads][head_dim], 16-B aligned.
+ *   slot_mapping  : int32 [num_tokens].
+ *   k_cache, v_cache : the pools, layouts above, num_blocks blocks each.
+ *   Source: nano-vllm hub page, "Attention + Triton Kernel" (slot mapping into
+ *   preallocated blocks); CSDN essay, first section (block table).
+ */
+int pa_store_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for a
+ * batch of this shape on the current device (split-context partial results).
+ * Returns 0 for shapes pa_decode would reject.
+ */
+size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size);
+
+/*
+ * pa_decode -- attention of one new query token per sequence over its whole
+ * paged context.
+ *
+ * For sequence b and query head h (kv head g = h / G), with n = context_lens[b]
+ * and K_b[j], V_b[j] the cached key/value of position j (read through
+ * block_table[b]):
+ *   s_j = scale * <q[b][h], K_b[j][g]>   for j < n
+ *   out[b][h] = sum_j exp(s_j - max s) V_b[j][g] / sum_j exp(s_j - max s)
+ * rounded to bf16 (nearest even) from fp32 accumulators.  n == 0 gives a zero
+ * row.  The new token must already be stored (pa_store_kv on the same stream).
+ * Long contexts are cut into chunks whose partial (max, sum, weighted V) states
+ * are merged; the result does not depend on the cut beyond rounding.
+ *
+ *   out           : bf16 [batch][num_q_heads][head_dim], 16-B aligned.
+ *   q             : bf16 [batch][num_q_heads][head_dim], 16-B aligned.
+ *   k_cache, v_cache, block_table : see above; max_blocks_per_seq = row length.
+ *   context_lens  : int32 [batch].
+ *   max_context_len : an upper bound of context_lens used to size the launch
+ *                   (must be <= max_blocks_per_seq*block_size).
+ *   scale         : the logit scale (e.g. 1/sqrt(head_dim)); finite.
+ *   workspace     : >= pa_decode_workspace_size(...) bytes of device memory,
+ *                   256-B aligned; its contents need no initialisation and are
+ *                   scratch after the call returns.
+ *   Source: CSDN essay, first and third sections; vLLM decode kernel
+ *   description in the same essay.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * pa_prefill -- causal varlen attention of prompt tokens over the paged cache.
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (q_len_b of
+ * them).  Query row i of sequence b is the token at position
+ * a = context_lens[b] - q_len_b + i and attends to the cached positions 0..a of
+ * the same sequence (bottom-right aligned causal mask, so a cached prefix is
+ * seen in full), with the same softmax formula as pa_decode.  The K/V of all
+ * context_lens[b] positions must already be in the cache.
+ *
+ *   out, q        : bf16 [total_q][num_q_heads][head_dim], 16-B aligned,
+ *                   total_q = cu_seqlens_q[batch].
+ *   cu_seqlens_q  : int32 [batch+1], non-decreasing, cu_seqlens_q[0] = 0.
+ *   context_lens  : int32 [batch].
+ *   max_seqlen_q  : an upper bound of q_len_b (sizes the launch).
+ *   Source: nano-vllm hub page, "Scheduler" (prefill fills the cache with the
+ *   prompt); CSDN essay, reading vLLM's attention module (prefill kernel).
+ */
+int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
+               const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
+               const void* k_cache, const void* v_cache, const int32_t* block_table,
+               int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+               void* stream);
+
+/* Name of a status code ("PA_OK", "PA_ERR_NULL_PTR", ...); never NULL. */
+const char* pa_status_string(int status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char* pa_last_error_detail(void);
+
+/*
+ * pa_validate_slots -- host-side check of a slot mapping (a debugging aid for
+ * the store's data preconditions).  host_slots is a HOST array of n slots.
+ * Returns PA_ERR_SLOT_RANGE if some slot is >= num_slots, PA_ERR_DUPLICATE_SLOT
+ * if two non-negative slots are equal, PA_OK otherwise.
+ */
+int pa_validate_slots(const int32_t* host_slots, int64_t n, int64_t num_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,203 @@
+"""Python binding of libpa.so, the gfx950 paged KV-cache attention library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors must be contiguous and live on the current HIP device; bf16
+arrays may be passed as torch.bfloat16 or as int16 bit views.  Calls are
+asynchronous on the current torch stream of the tensors' device (or on the
+stream passed in).  The library must be built first
+(``python -m paged_kv_cache_237_amd.build`` or ``__graft_entry__.build()``);
+importing succeeds without it, and the first call raises if it is missing.
+
+Cache layout (see include/pa.h): K cache bf16 [num_blocks, Hkv, 16, 256, 8],
+V cache bf16 [num_blocks, Hkv, 256, 128].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+BLOCK_SIZE = 256
+HEAD_DIM = 128
+K_CHUNK = 8
+
+PA_OK = 0
+STATUS_NAMES = {
+    0: "PA_OK", -1: "PA_ERR_NULL_PTR", -2: "PA_ERR_BAD_SHAPE", -3: "PA_ERR_UNSUPPORTED",
+    -4: "PA_ERR_ALIGN", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP", -7: "PA_ERR_SLOT_RANGE",
+    -8: "PA_ERR_DUPLICATE_SLOT",
+}
+
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_prefill",
+           "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (torch's HIP runtime is loaded first so that libpa
+    binds to that same runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m paged_kv_cache_237_amd.build` first")
+        l = ctypes.CDLL(LIB_PATH)
+        l.pa_store_kv.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
+        l.pa_store_kv.restype = ctypes.c_int
+        l.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+        l.pa_decode_workspace_size.restype = _sz
+        l.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i64, _f32, _vp, _sz, _vp]
+        l.pa_decode.restype = ctypes.c_int
+        l.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _i64, _f32, _vp]
+        l.pa_prefill.restype = ctypes.c_int
+        l.pa_status_string.argtypes = [ctypes.c_int]
+        l.pa_status_string.restype = ctypes.c_char_p
+        l.pa_last_error_detail.argtypes = []
+        l.pa_last_error_detail.restype = ctypes.c_char_p
+        l.pa_validate_slots.argtypes = [_vp, _i64, _i64]
+        l.pa_validate_slots.restype = ctypes.c_int
+        _lib = l
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PAError(status, lib().pa_last_error_detail().decode())
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+_I32 = (torch.int32,)
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def alloc_cache(num_blocks: int, num_kv_heads: int, device="cuda", fill_bits: Optional[int] = None):
+    """Allocate a (K, V) cache pair as bf16 tensors in the library layout,
+    optionally filled with a bf16 bit pattern."""
+    k = torch.empty((num_blocks, num_kv_heads, HEAD_DIM // K_CHUNK, BLOCK_SIZE, K_CHUNK),
+                    dtype=torch.bfloat16, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE, HEAD_DIM), dtype=torch.bfloat16,
+                    device=device)
+    if fill_bits is not None:
+        fb = fill_bits - 0x10000 if fill_bits >= 0x8000 else fill_bits
+        k.view(torch.int16).fill_(fb)
+        v.view(torch.int16).fill_(fb)
+    return k, v
+
+
+def _cache_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    if k_cache.dim() != 5 or tuple(k_cache.shape[2:]) != (HEAD_DIM // K_CHUNK, BLOCK_SIZE, K_CHUNK):
+        raise ValueError(f"k_cache must be [num_blocks, Hkv, 16, 256, 8], got {tuple(k_cache.shape)}")
+    nb, hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    if tuple(v_cache.shape) != (nb, hkv, BLOCK_SIZE, HEAD_DIM):
+        raise ValueError(f"v_cache must be [{nb}, {hkv}, 256, 128], got {tuple(v_cache.shape)}")
+    return nb, hkv
+
+
+def store_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """pa_store_kv: k_new/v_new [N, Hkv, 128], slot_mapping int32 [N]."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    n = int(slot_mapping.shape[0])
+    if tuple(k_new.shape) != (n, hkv, HEAD_DIM) or tuple(v_new.shape) != (n, hkv, HEAD_DIM):
+        raise ValueError("k_new/v_new must be [N, Hkv, 128] matching slot_mapping and the cache")
+    _check(lib().pa_store_kv(
+        _dev(k_new, "k_new", _BF16), _dev(v_new, "v_new", _BF16),
+        _dev(slot_mapping, "slot_mapping", _I32), n,
+        _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16), nb, BLOCK_SIZE, hkv,
+        HEAD_DIM, _stream(k_cache, stream)))
+
+
+def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int) -> int:
+    n = lib().pa_decode_workspace_size(batch, num_q_heads, num_kv_heads, HEAD_DIM, BLOCK_SIZE)
+    if n == 0 and batch > 0:
+        raise PAError(-6, "pa_decode_workspace_size returned 0: " +
+                      lib().pa_last_error_detail().decode())
+    return int(n)
+
+
+def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, device="cuda"):
+    n = decode_workspace_size(batch, num_q_heads, num_kv_heads)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
+           scale: float, workspace, stream=None) -> None:
+    """pa_decode: q/out [B, Hq, 128], block_table int32 [B, max_blocks_per_seq],
+    context_lens int32 [B]."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    b, hq, d = (int(x) for x in q.shape)
+    if tuple(out.shape) != (b, hq, d) or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("shape mismatch between q, out and block_table")
+    if tuple(context_lens.shape) != (b,):
+        raise ValueError("context_lens must be [B]")
+    _check(lib().pa_decode(
+        _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(k_cache, "k_cache", _BF16),
+        _dev(v_cache, "v_cache", _BF16), _dev(block_table, "block_table", _I32),
+        int(block_table.shape[1]), _dev(context_lens, "context_lens", _I32), b,
+        int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        _dev(workspace, "workspace", (torch.uint8, torch.float32, torch.int32)),
+        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+
+
+def prefill(out, q, cu_seqlens_q, context_lens, max_seqlen_q: int, k_cache, v_cache,
+            block_table, scale: float, stream=None) -> None:
+    """pa_prefill: q/out [total_q, Hq, 128], cu_seqlens_q int32 [B+1],
+    context_lens int32 [B], block_table int32 [B, max_blocks_per_seq]."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    tq, hq, d = (int(x) for x in q.shape)
+    b = int(context_lens.shape[0])
+    if tuple(out.shape) != (tq, hq, d) or tuple(cu_seqlens_q.shape) != (b + 1,):
+        raise ValueError("shape mismatch between q, out, cu_seqlens_q and context_lens")
+    if block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    _check(lib().pa_prefill(
+        _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(cu_seqlens_q, "cu_seqlens_q", _I32),
+        _dev(context_lens, "context_lens", _I32), b, int(max_seqlen_q),
+        _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(block_table, "block_table", _I32), int(block_table.shape[1]), hq, hkv, d,
+        BLOCK_SIZE, nb, float(scale), _stream(q, stream)))
+
+
+def validate_slots(slots_host, num_slots: int) -> int:
+    """pa_validate_slots on a host int32 array; returns the status code."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(slots_host, dtype=np.int32))
+    return int(lib().pa_validate_slots(arr.ctypes.data if arr.size else None, arr.size, num_slots))

@@ -1,0 +1,294 @@
+// C-ABI entry points of libpa: host-side argument checks, launch sizing and
+// error reporting.  Declarations and the contract of every call are in
+// include/pa.h.  Nothing here allocates device memory or keeps state beyond a
+// per-device cache of the compute-unit count.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "pa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const std::string& msg) {
+  g_detail = msg;
+  return code;
+}
+
+int ok() {
+  g_detail.clear();
+  return PA_OK;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                              hipGetErrorString(e) + ")");
+}
+
+// Compute units of the current device (cached per device).
+int current_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::mutex mu;
+  static std::vector<int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && size_t(dev) < cache.size() && cache[dev] > 0) {
+    *cus = cache[dev];
+    return PA_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+  if (n <= 0) return fail(PA_ERR_HIP, "device reports no compute units");
+  if (size_t(dev) >= cache.size()) cache.resize(size_t(dev) + 1, 0);
+  cache[dev] = n;
+  *cus = n;
+  return PA_OK;
+}
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int check_geometry(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int* group) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0)
+    return fail(PA_ERR_BAD_SHAPE, "head counts must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_BAD_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  if (head_dim != PA_HEAD_DIM) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_UNSUPPORTED, "block_size must be 256");
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_group(g))
+    return fail(PA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be 1, 2, 4 or 8");
+  *group = g;
+  return PA_OK;
+}
+
+int64_t decode_waves(int cus, int32_t batch, int32_t num_kv_heads, int32_t max_context_len) {
+  const int64_t tiles_upper =
+      int64_t(batch) * num_kv_heads * ((int64_t(max_context_len) + pa::kTile - 1) / pa::kTile);
+  const int64_t w = int64_t(cus) * pa::kDecodeWavesPerCU;
+  return std::max<int64_t>(1, std::min(w, tiles_upper));
+}
+
+size_t decode_ws_bytes(int32_t batch, int32_t num_kv_heads, int group, int64_t waves) {
+  const int64_t records = int64_t(batch) * num_kv_heads + waves;
+  const size_t bytes = size_t(records) * size_t(pa::partial_floats(group)) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL_PTR: return "PA_ERR_NULL_PTR";
+    case PA_ERR_BAD_SHAPE: return "PA_ERR_BAD_SHAPE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_SLOT_RANGE: return "PA_ERR_SLOT_RANGE";
+    case PA_ERR_DUPLICATE_SLOT: return "PA_ERR_DUPLICATE_SLOT";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error_detail(void) { return g_detail.c_str(); }
+
+int pa_validate_slots(const int32_t* host_slots, int64_t n, int64_t num_slots) {
+  try {
+    if (n < 0 || num_slots < 0) return fail(PA_ERR_BAD_SHAPE, "negative size");
+    if (n == 0) return ok();
+    if (host_slots == nullptr) return fail(PA_ERR_NULL_PTR, "host_slots is NULL");
+    std::vector<int32_t> s;
+    s.reserve(size_t(n));
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t v = host_slots[i];
+      if (v < 0) continue;
+      if (int64_t(v) >= num_slots)
+        return fail(PA_ERR_SLOT_RANGE, "slot_mapping[" + std::to_string(i) + "] = " +
+                                           std::to_string(v) + " >= " + std::to_string(num_slots));
+      s.push_back(v);
+    }
+    std::sort(s.begin(), s.end());
+    for (size_t i = 1; i < s.size(); ++i)
+      if (s[i] == s[i - 1])
+        return fail(PA_ERR_DUPLICATE_SLOT, "slot " + std::to_string(s[i]) + " appears twice");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_BAD_SHAPE, "host allocation failed");
+  }
+}
+
+int pa_store_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  try {
+    if (num_tokens < 0) return fail(PA_ERR_BAD_SHAPE, "num_tokens < 0");
+    if (num_kv_heads <= 0) return fail(PA_ERR_BAD_SHAPE, "num_kv_heads must be positive");
+    if (head_dim != PA_HEAD_DIM) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+    if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_UNSUPPORTED, "block_size must be 256");
+    if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
+    if (num_blocks > (int64_t(INT32_MAX) + 1) / PA_BLOCK_SIZE)
+      return fail(PA_ERR_BAD_SHAPE, "pool has more slots than an int32 slot can address");
+    if (num_kv_heads > 65535) return fail(PA_ERR_BAD_SHAPE, "num_kv_heads > 65535");
+    if (num_tokens == 0) return ok();
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+      return fail(PA_ERR_NULL_PTR, "pa_store_kv: a pointer argument is NULL");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(slot_mapping, 4))
+      return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, slot_mapping 4-byte");
+    if ((num_tokens + pa::kTile - 1) / pa::kTile > INT32_MAX)
+      return fail(PA_ERR_BAD_SHAPE, "num_tokens too large");
+    pa::StoreArgs a;
+    a.k_new = static_cast<const uint4*>(k_new);
+    a.v_new = static_cast<const uint4*>(v_new);
+    a.slots = slot_mapping;
+    a.k_cache = static_cast<uint4*>(k_cache);
+    a.v_cache = static_cast<uint4*>(v_cache);
+    a.n = num_tokens;
+    a.num_slots = num_blocks * PA_BLOCK_SIZE;
+    a.hkv = num_kv_heads;
+    const hipError_t e = pa::launch_store_kv(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "store_kv launch");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size) {
+  try {
+    int group = 0;
+    if (batch < 0) return 0;
+    if (check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group) != PA_OK) return 0;
+    int cus = 0;
+    if (current_cus(&cus) != PA_OK) return 0;
+    const int64_t waves = int64_t(cus) * pa::kDecodeWavesPerCU;
+    return decode_ws_bytes(batch, num_kv_heads, group, waves);
+  } catch (...) {
+    return 0;
+  }
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  try {
+    if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
+    int group = 0;
+    int r = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group);
+    if (r != PA_OK) return r;
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq must be positive");
+    if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
+    if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE)
+      return fail(PA_ERR_BAD_SHAPE, "max_context_len outside [0, max_blocks_per_seq*block_size]");
+    if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
+    if (batch == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens)
+      return fail(PA_ERR_NULL_PTR, "pa_decode: a pointer argument is NULL");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(context_lens, 4))
+      return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, int32 arrays 4-byte");
+    // every tile index of the flattened work list must fit an int
+    if (int64_t(batch) * num_kv_heads * max_blocks_per_seq * (PA_BLOCK_SIZE / pa::kTile) >
+        int64_t(INT32_MAX) / 2)
+      return fail(PA_ERR_BAD_SHAPE, "batch * num_kv_heads * max_blocks_per_seq too large");
+    int cus = 0;
+    r = current_cus(&cus);
+    if (r != PA_OK) return r;
+    const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len);
+    const size_t need = decode_ws_bytes(batch, num_kv_heads, group, waves);
+    if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 16)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                        std::to_string(workspace_bytes));
+    pa::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint4*>(k_cache);
+    a.v_cache = static_cast<const uint4*>(v_cache);
+    a.block_table = block_table;
+    a.ctx_lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    a.ws = static_cast<float*>(workspace);
+    a.num_blocks = num_blocks;
+    a.batch = batch;
+    a.hkv = num_kv_heads;
+    a.mbps = max_blocks_per_seq;
+    a.n_waves = int(waves);
+    a.scale_log2 = float(double(scale) * 1.4426950408889634);
+    const hipError_t e = pa::launch_decode(a, group, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
+               const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
+               const void* k_cache, const void* v_cache, const int32_t* block_table,
+               int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+               void* stream) {
+  try {
+    if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
+    int group = 0;
+    int r = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group);
+    if (r != PA_OK) return r;
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq must be positive");
+    if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
+    if (max_seqlen_q < 0 || int64_t(max_seqlen_q) > int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE)
+      return fail(PA_ERR_BAD_SHAPE, "max_seqlen_q outside [0, max_blocks_per_seq*block_size]");
+    if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
+    if (batch == 0 || max_seqlen_q == 0) return ok();
+    if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_table)
+      return fail(PA_ERR_NULL_PTR, "pa_prefill: a pointer argument is NULL");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
+      return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, int32 arrays 4-byte");
+    pa::PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint4*>(k_cache);
+    a.v_cache = static_cast<const uint4*>(v_cache);
+    a.block_table = block_table;
+    a.cu_q = cu_seqlens_q;
+    a.ctx_lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    a.num_blocks = num_blocks;
+    a.batch = batch;
+    a.hq = num_q_heads;
+    a.hkv = num_kv_heads;
+    a.mbps = max_blocks_per_seq;
+    a.max_q = max_seqlen_q;
+    a.scale_log2 = float(double(scale) * 1.4426950408889634);
+    const hipError_t e = pa::launch_prefill(a, group, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available");
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the kernel
+// translation units.  Launchers validate nothing: api.cpp has already checked
+// every argument.  Each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlock = 256;      // tokens per cache block
+constexpr int kDim = 128;        // head dim
+constexpr int kChunks = kDim / 8;  // 16-byte chunks per row
+constexpr int kTile = 64;        // decode tile: one token per lane
+
+// Partial-state record of one decode work piece: G rows of D fp32 weighted
+// values, then G maxima, then G sums (floats).
+__host__ __device__ constexpr int partial_floats(int g) { return g * (kDim + 2); }
+
+struct StoreArgs {
+  const uint4* k_new;
+  const uint4* v_new;
+  const int32_t* slots;
+  uint4* k_cache;
+  uint4* v_cache;
+  int64_t n;
+  int64_t num_slots;
+  int hkv;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint4* k_cache;
+  const uint4* v_cache;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  uint16_t* out;
+  float* ws;
+  int64_t num_blocks;
+  int batch;
+  int hkv;
+  int mbps;        // max_blocks_per_seq
+  int n_waves;     // waves in the split-context grid
+  float scale_log2;  // scale * log2(e)
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint4* k_cache;
+  const uint4* v_cache;
+  const int32_t* block_table;
+  const int32_t* cu_q;
+  const int32_t* ctx_lens;
+  uint16_t* out;
+  int64_t num_blocks;
+  int batch;
+  int hq;
+  int hkv;
+  int mbps;
+  int max_q;
+  float scale_log2;
+};
+
+// Waves per CU the decode grid is sized for.
+constexpr int kDecodeWavesPerCU = 8;
+
+hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t s);
+
+}  // namespace pa
