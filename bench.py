@@ -91,9 +91,10 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int):
     return wall * 1e3 / steps, dec, sto
 
 
-def cpu_baseline(case: wl.PagedCase, budget_s: float = 12.0) -> dict:
-    """The oracle as it stands, on a bounded sample of the same workload: whole
-    sequences in batch order until about budget_s of CPU work."""
+def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload: whole sequences in batch order (wrapping around to the
+    first sequence again) until about budget_s of oracle time."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -101,24 +102,28 @@ def cpu_baseline(case: wl.PagedCase, budget_s: float = 12.0) -> dict:
     from paged_harness import oracle_pools  # noqa: E402
 
     q = wl.bits_to_numpy(case.q_all())
+    pools = {}
     done_ctx, done_seqs, spent = 0, 0, 0.0
-    for b in range(case.batch):
-        kp, vp = oracle_pools(case, [b], poison=False)
+    while spent < budget_s:
+        b = done_seqs % case.batch
+        if b not in pools:
+            pools[b] = oracle_pools(case, [b], poison=False)
+        kp, vp = pools[b]
         t0 = time.perf_counter()
         oracle.decode_seq(q[b], kp, vp, case.block_table[b], int(case.context_lens[b]), case.scale)
         spent += time.perf_counter() - t0
         done_ctx += int(case.context_lens[b])
         done_seqs += 1
-        del kp, vp
-        if spent >= budget_s:
-            break
+        if len(pools) > 8:
+            pools.pop(next(iter(pools)))
     bytes_done = done_ctx * case.num_kv_heads * case.head_dim * 2 * 2
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": bytes_done / spent / 1e9, "unit": "GB/s", "cores": int(threads),
+    return {"value": round(bytes_done / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{case.name}: oracle decode of the first {done_seqs} of {case.batch} "
-                      f"sequences ({done_ctx} attended tokens x {case.num_q_heads} q heads), "
-                      f"{spent:.1f} s; tokens/s {done_ctx / spent:.0f}"}
+            "sample": f"{case.name}: float64 oracle decode of {done_seqs} whole sequences in "
+                      f"batch order ({done_ctx} attended tokens x {case.num_q_heads} q heads, "
+                      f"{spent:.1f} s of oracle time; {done_ctx / spent:.0f} attended tokens/s); "
+                      f"GB/s counts the same algorithmic K/V bytes as the GPU figure"}
 
 
 def main(argv=None):

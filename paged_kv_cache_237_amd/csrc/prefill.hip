@@ -1,9 +1,318 @@
-// Causal varlen prefill over the paged cache (gfx950): placeholder until the
-// MFMA kernel lands; reports "not supported".
+// Causal varlen prefill attention over the paged cache, on gfx950 MFMA.
+//
+// What it computes (nano-vllm hub page, "Scheduler": prefill runs the prompt
+// and fills the cache; CSDN essay comparing nanoVLLM and vLLM, third section:
+// exact attention in on-chip tiles, and the vLLM reading section: prefill is
+// the compute-bound phase with its own kernel): for query row i of sequence b,
+// at position a = ctx_b - q_len_b + i, o = softmax(scale * q K[0..a]^T) V[0..a]
+// per head, with K/V read through the sequence's block table.
+//
+// One workgroup = 4 waves = 128 query rows (G heads x 128/G positions) of one
+// (sequence, kv head), so every K/V tile staged in LDS serves all G heads.
+// Tiles of 64 keys never straddle a 256-token block (one table lookup each).
+// Per wave and tile (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   S^T = K Q^T : A = K rows from LDS (16 B per lane, the cache's 8-dim chunks),
+//                 B = the wave's 32 query rows, held in registers for the whole
+//                 loop.  The accumulator then holds one query row per lane
+//                 (column) and 16 keys per register set, so row max and row
+//                 sum are in-lane plus one exchange with lane^32.
+//   O  = P V    : A = bf16(P) taken straight from the S^T accumulator -- the
+//                 contraction runs over keys in the accumulator's register
+//                 order, and V is read from a transposed LDS copy ([dim][key])
+//                 in that same key order, so P never moves between lanes.
+// Online softmax in the log2 domain (scale*log2 e folded into one FMA) with a
+// lazy rescale: the reference max only moves when a row's max grows by more
+// than 2^8, so O is rescaled rarely.  Tiles entirely above a wave's diagonal
+// are skipped; only tiles crossing it are masked.  Keys past the context are
+// loaded as zeros through raw-buffer range checks (the cache may hold NaN
+// patterns there).  Workgroups are dispatched longest-first: grid z counts
+// query blocks from the end of each sequence.
+#include <math.h>
+
+#include "pa_device.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
 
-hipError_t launch_prefill(const PrefillArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kRowsPerWG = 128;  // query rows (head, position) per workgroup
+constexpr int kKeys = 64;        // keys per K/V tile
+constexpr int kVtStride = 68;    // bf16 per transposed-V row in LDS (64 keys + pad)
+constexpr float kLazyRescale = 8.f;  // log2 headroom before O is rescaled
+
+struct __align__(16) PrefillSmem {
+  uint4 k[kChunks * kKeys];              // [chunk][key] 16-byte chunks: 16 KiB
+  uint16_t vt[kDim * kVtStride];         // [dim][key] bf16: 17 KiB
+  float rowf[4][32];                     // per-wave row factors
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int QB = kRowsPerWG / G;  // positions per workgroup
+  __shared__ PrefillSmem sm;
+
+  const int b = blockIdx.x;
+  const int g = blockIdx.y;
+  const int jrev = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  const int q0 = a.cu_q[b];
+  const int qlen = max(0, a.cu_q[b + 1] - q0);
+  const int cap = a.mbps * kBlock;
+  const int ctx = min(max(a.ctx_lens[b], 0), cap);
+  const int nqb = (qlen + QB - 1) / QB;
+  if (jrev >= nqb) return;
+  const int p0 = (nqb - 1 - jrev) * QB;
+  const int shift = ctx - qlen;  // absolute position of query row 0
+
+  // This lane's query row (the S^T column it owns): head hl, position pos.
+  const int R = w * 32 + col;
+  const int hl = R / QB;
+  const int pos = p0 + R % QB;
+  const int head = g * G + hl;
+  const bool row_ok = pos < qlen;
+  const int a_pos = row_ok ? min(shift + pos, ctx - 1) : -1;  // last visible key
+
+  // Wave-uniform key range of this wave's rows.
+  int amax = a_pos, amin = a_pos;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    amax = max(amax, __shfl_xor(amax, d, 64));
+    amin = min(amin, __shfl_xor(amin, d, 64));
+  }
+  amax = __builtin_amdgcn_readfirstlane(amax);
+  amin = __builtin_amdgcn_readfirstlane(amin);
+
+  // Q^T operand: dims 16*ks + 8*half .. +7 of the lane's row, 8 k-steps.
+  bf16x8_t qop[8];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        a.q + (int64_t(q0) + (row_ok ? pos : 0)) * (int64_t(a.hq) * kDim) + int64_t(head) * kDim);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(row_ok ? qrow[2 * ks + half] : zero4());
+  }
+
+  // Keys the whole workgroup needs.
+  const int last_row = min(p0 + QB, qlen) - 1;
+  const int kend = min(shift + last_row + 1, ctx);
+  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+
+  const float c = a.scale_log2;
+  f32x16_t o[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[n][r] = 0.f;
+  float m = -INFINITY;  // running reference max of the lane's row (log2 units)
+  float l = 0.f;        // partial row sum over this lane's keys
+
+  const int32_t* table = a.block_table + int64_t(b) * a.mbps;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int key0 = t * kKeys;
+    const int phys = table[key0 / kBlock];
+    const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
+    const int valid = ok ? min(kKeys, ctx - key0) : 0;
+    const int r0 = key0 % kBlock;
+    const int64_t bh = (ok ? int64_t(phys) : 0) * a.hkv + g;
+
+    // ---- stage K (as is) and V (transposed) of this tile in LDS ----------
+    {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + bh * (kChunks * kBlock), 65536u);
+      const __amdgpu_buffer_rsrc_t rv =
+          make_rsrc(a.v_cache + bh * (kBlock * kChunks), uint32_t(r0 + valid) * 256u);
+      uint4 kx[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = tid + 256 * j;
+        const int ch = i >> 6, row = i & 63;
+        const uint32_t off = row < valid ? uint32_t(ch * kBlock + r0 + row) * 16u : kOutOfRange;
+        kx[j] = buf_load16(rk, off, 0u);
+      }
+      const int kp = tid & 31;  // key pair
+      uint4 va[2], vb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ch = (tid >> 5) + 8 * j;
+        const uint32_t off = uint32_t((r0 + 2 * kp) * kChunks + ch) * 16u;
+        va[j] = buf_load16(rv, off, 0u);
+        vb[j] = buf_load16(rv, off + 256u, 0u);
+      }
+      __syncthreads();  // previous tile fully consumed
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.k[tid + 256 * j] = kx[j];
+      uint32_t* vt32 = reinterpret_cast<uint32_t*>(sm.vt);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ch = (tid >> 5) + 8 * j;
+        const uint32_t r0w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+        const uint32_t r1w[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = ch * 8 + 2 * e;
+          vt32[(d * kVtStride) / 2 + kp] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x05040100u);
+          vt32[((d + 1) * kVtStride) / 2 + kp] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x07060302u);
+        }
+      }
+      __syncthreads();
+    }
+
+    if (key0 > amax) continue;  // every key of the tile is above this wave's diagonal
+
+    // ---- S^T = K Q^T : two 32-key subtiles --------------------------------
+    f32x16_t s[2];
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[ms][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t ka = as_bf16x8(sm.k[(2 * ks + half) * kKeys + 32 * ms + col]);
+        s[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], s[ms], 0, 0, 0);
+      }
+    }
+
+    // ---- mask keys past the row's position (diagonal / tail tiles) -------
+    if (key0 + kKeys - 1 > amin) {
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * ms + (r & 3) + 8 * (r >> 2) + 4 * half;
+          s[ms][r] = key <= a_pos ? s[ms][r] : -INFINITY;
+        }
+    }
+
+    // ---- online softmax with lazy rescale ---------------------------------
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[ms][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+    const float mnew = fmaxf(m, mt);
+    const bool need = mnew > m + kLazyRescale;  // also true for the first finite max
+    if (__ballot(need) != 0) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
+      if (need) {
+        l *= alpha;
+        m = mnew;
+      }
+      if (half == 0) sm.rowf[w][col] = alpha;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 al = *reinterpret_cast<const float4*>(&sm.rowf[w][8 * qd + 4 * half]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          o[n][4 * qd + 0] *= al.x;
+          o[n][4 * qd + 1] *= al.y;
+          o[n][4 * qd + 2] *= al.z;
+          o[n][4 * qd + 3] *= al.w;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    const float mref = m == -INFINITY ? 0.f : m;
+
+    // ---- P = 2^(c s - m) as bf16 A operands, row sums --------------------
+    // The row sum adds the bf16-rounded weights the MFMA actually uses, so
+    // the output is a convex combination of V rows with consistently rounded
+    // weights (a dominant weight cancels exactly in O / l).
+    bf16x8_t pop[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float pf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + e], c, -mref));
+      const uint4 pb = pack8(pf);
+      l += (bf16_lo(pb.x) + bf16_hi(pb.x)) + (bf16_lo(pb.y) + bf16_hi(pb.y)) +
+           (bf16_lo(pb.z) + bf16_hi(pb.z)) + (bf16_lo(pb.w) + bf16_hi(pb.w));
+      pop[ks] = as_bf16x8(pb);
+    }
+
+    // ---- O += P V ------------------------------------------------------------
+    const uint32_t* vt32 = reinterpret_cast<const uint32_t*>(sm.vt);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int dim = 32 * n + col;
+        const int base = (dim * kVtStride + 16 * ks + 4 * half) / 2;  // in dwords
+        const uint2 lo = *reinterpret_cast<const uint2*>(vt32 + base);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vt32 + base + 4);
+        const bf16x8_t vop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], vop, o[n], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: O / l -> bf16, staged through LDS for 16-byte stores -------
+  __syncthreads();  // K/V buffers are reused below
+  const float ltot = l + __shfl_xor(l, 32, 64);
+  if (half == 0) sm.rowf[w][col] = ltot > 0.f ? 1.f / ltot : 0.f;
+  __builtin_amdgcn_wave_barrier();
+  uint16_t* stage = reinterpret_cast<uint16_t*>(sm.k) + w * (32 * kDim);  // [32 rows][128]
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const float4 inv = *reinterpret_cast<const float4*>(&sm.rowf[w][8 * qd + 4 * half]);
+    const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * qd + 4 * half + i;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const __bf16 v = static_cast<__bf16>(o[n][4 * qd + i] * iv[i]);
+        stage[row * kDim + 32 * n + col] = __builtin_bit_cast(uint16_t, v);
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // 32 rows x 16 chunks = 512 chunks, 8 per lane
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int idx = lane + 64 * j;
+    const int row = idx >> 4, ch = idx & 15;
+    const int Rr = w * 32 + row;
+    const int p = p0 + Rr % QB;
+    if (p < qlen) {
+      const int hh = g * G + Rr / QB;
+      const uint4 val = reinterpret_cast<const uint4*>(stage)[row * kChunks + ch];
+      uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t(q0) + p) * (int64_t(a.hq) * kDim) +
+                                            int64_t(hh) * kDim);
+      dst[ch] = val;
+    }
+  }
+}
+
+template <int G>
+static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
+  constexpr int QB = kRowsPerWG / G;
+  const int nqb = (a.max_q + QB - 1) / QB;
+  const dim3 grid(unsigned(a.batch), unsigned(a.hkv), unsigned(nqb));
+  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_prefill_g<1>(a, s);
+    case 2: return launch_prefill_g<2>(a, s);
+    case 4: return launch_prefill_g<4>(a, s);
+    case 8: return launch_prefill_g<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 }  // namespace pa

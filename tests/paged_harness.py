@@ -118,6 +118,41 @@ def compare(got: np.ndarray, ref: np.ndarray, what: str, stress: bool = False) -
     return stats
 
 
+def bf16_weight_bound(q_bits, k_bits, v_bits, scale, last_pos):
+    """Per-element error bound of an attention whose softmax weights are
+    rounded to bf16 (relative error <= 2^-8 each) and then normalised by the
+    sum of the rounded weights: |d o_d| <= 2^-8 * sum_j w_j |v_jd - o_d| to
+    first order (w, o from the float64 reference).  q_bits [R, D] bf16 bits of
+    one head; k_bits, v_bits [n, D]; row r sees keys 0..last_pos[r]."""
+    q = oracle.bf16_to_f64(q_bits)
+    k = oracle.bf16_to_f64(k_bits)
+    v = oracle.bf16_to_f64(v_bits)
+    out = np.zeros((q.shape[0], v.shape[1]))
+    for lo in range(0, q.shape[0], 64):
+        hi = min(q.shape[0], lo + 64)
+        s = (q[lo:hi] @ k.T) * scale
+        j = np.arange(k.shape[0])[None, :]
+        s = np.where(j <= np.asarray(last_pos[lo:hi])[:, None], s, -np.inf)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        o = w @ v
+        out[lo:hi] = np.einsum("rj,rjd->rd", w, np.abs(v[None, :, :] - o[:, None, :]))
+    return 2.0 ** -8 * 1.01 * out
+
+
+def compare_bounded(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str) -> dict:
+    """|err| <= half a bf16 ulp of the reference (output rounding) + a derived
+    per-element bound + 1e-5 (fp32 accumulation)."""
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8)
+    slack = err - (half_ulp + bound + 1e-5)
+    stats = {"max_abs": float(err.max(initial=0.0)), "mean_abs": float(err.mean()),
+             "worst_margin": float(slack.max(initial=-1.0))}
+    assert not (slack > 0).any(), f"{what}: {int((slack > 0).sum())} elements beyond bound, {stats}"
+    return stats
+
+
 def compare_pools_bytes(dev: DeviceCase, kp: np.ndarray, vp: np.ndarray, blocks=None):
     """Bytewise equality of device pools with host pools (all blocks, or the
     listed physical blocks)."""

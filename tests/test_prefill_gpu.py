@@ -1,0 +1,120 @@
+"""pa_prefill on the GPU against the float64 oracle: the 8 x 2048 causal
+workload, ragged varlen batches with every grouped-head ratio, prompts with a
+cached prefix (bottom-right causal alignment), stress inputs, and
+consistency with pa_decode (row i of a prompt = decode at length i+1)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_237_amd as pa
+import workloads as wl
+from paged_harness import (bf16_out_to_f64, bf16_weight_bound, compare, compare_bounded,
+                            oracle_pools, place)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(dev):
+    case = dev.case
+    pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+    out = torch.full((case.total_q_rows, case.num_q_heads, case.head_dim), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
+    pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache, dev.v_cache,
+               dev.block_table, case.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(case, stress=False, seqs_full=None, heads_sampled=None):
+    print(f"[prefill] {case.name} B={case.batch} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+          f"q_lens={case.q_lens.tolist()[:10]} ctx={case.context_lens.tolist()[:10]}", flush=True)
+    dev = place(case)
+    out = bf16_out_to_f64(run_prefill(dev))
+    kp, vp = oracle_pools(case)
+    q = wl.bits_to_numpy(case.q_all())
+    got, ref = [], []
+    for b in range(case.batch):
+        lo, hi = int(case.q_offsets[b]), int(case.q_offsets[b + 1])
+        if hi == lo:
+            continue
+        heads = None
+        if seqs_full is not None and b not in seqs_full:
+            heads = heads_sampled
+        r = oracle.prefill_seq(q[lo:hi], kp, vp, case.block_table[b], int(case.context_lens[b]),
+                               case.scale, heads=heads)
+        hs = range(case.num_q_heads) if heads is None else heads
+        for h in hs:
+            got.append(out[lo:hi, h])
+            ref.append(r[:, h])
+    return compare(np.concatenate(got), np.concatenate(ref), case.name, stress=stress)
+
+
+def test_prefill_8x2048():
+    check(wl.prefill_8x2048(), seqs_full={0, 7}, heads_sampled=[1, 6, 11])
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (4, 1)])
+def test_prefill_ragged_all_group_sizes(hq, hkv):
+    lens = [1, 255, 256, 257, 300, 64, 65, 127, 1100]
+    check(wl.make_case(f"ragged_{hq}_{hkv}", "prefill", 40 + hq, lens, hq, hkv))
+
+
+def test_prefill_with_cached_prefix():
+    ctx = [300, 1000, 4097, 64, 513, 2]
+    qlens = [1, 100, 257, 64, 1, 2]
+    check(wl.make_case("prefix", "prefill", 41, ctx, 16, 8, q_lens=qlens))
+
+
+def test_prefill_stress_peaked_softmax():
+    """q scaled by 32: a sharply peaked softmax with |o| up to |v|.  The MFMA
+    takes the softmax weights in bf16, so the bar is the error bound derived
+    from that rounding (see bf16_weight_bound) plus output rounding."""
+    case = wl.make_case("stress", "prefill", 42, [5, 300, 700], 16, 8, q_mult=32.0)
+    dev = place(case)
+    out = bf16_out_to_f64(run_prefill(dev))
+    kp, vp = oracle_pools(case)
+    q = wl.bits_to_numpy(case.q_all())
+    for b in range(case.batch):
+        lo, hi = int(case.q_offsets[b]), int(case.q_offsets[b + 1])
+        n = int(case.context_lens[b])
+        ref = oracle.prefill_seq(q[lo:hi], kp, vp, case.block_table[b], n, case.scale)
+        kb, vb = oracle.gather_seq(kp, vp, case.block_table[b], n)
+        last = n - (hi - lo) + np.arange(hi - lo)
+        for h in range(case.num_q_heads):
+            g = h // case.group
+            bound = bf16_weight_bound(q[lo:hi, h], kb[:, g], vb[:, g], case.scale, last)
+            compare_bounded(out[lo:hi, h], ref[:, h], bound, f"stress seq {b} head {h}")
+
+
+def test_prefill_empty_sequences():
+    case = wl.make_case("empty", "prefill", 43, [0, 7, 0, 129], 16, 8)
+    check(case)
+
+
+def test_prefill_rows_match_decode():
+    """Prefill row i of a sequence equals decode of that row's query over the
+    first i+1 cached tokens (both within the parity bar of the oracle, and
+    close to each other)."""
+    n = 777
+    case = wl.make_case("rowdec", "prefill", 44, [n], 32, 8)
+    dev = place(case)
+    pre = run_prefill(dev)
+    rows = [0, 1, 63, 64, 255, 256, 500, n - 1]
+    q = dev.q[rows].contiguous()
+    ctx = torch.tensor([r + 1 for r in rows], dtype=torch.int32, device="cuda")
+    table = dev.block_table.expand(len(rows), -1).contiguous()
+    out = torch.empty_like(q, dtype=torch.bfloat16)
+    ws = pa.alloc_decode_workspace(len(rows), 32, 8)
+    pa.decode(out, q, dev.k_cache, dev.v_cache, table, ctx, n, case.scale, ws)
+    torch.cuda.synchronize()
+    d = bf16_out_to_f64(out)
+    p = bf16_out_to_f64(pre[rows])
+    assert np.abs(d - p).max() <= 2 * 1.5e-2
+    kp, vp = oracle_pools(case)
+    qb = wl.bits_to_numpy(case.q_all())
+    ref = np.stack([oracle.decode_seq(qb[r], kp, vp, case.block_table[0], r + 1, case.scale)
+                    for r in rows])
+    compare(d, ref, "decode rows")
+    compare(p, ref, "prefill rows")
