@@ -91,6 +91,62 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int):
     return wall * 1e3 / steps, dec, sto
 
 
+def prefill_flops(case: wl.PagedCase) -> int:
+    """Causal FLOPs of one pa_prefill: 4*D per (query row, visible key) pair
+    per query head (q.k and p.v, a multiply and an add each)."""
+    pairs = 0
+    for b in range(case.batch):
+        ql, n = int(case.q_lens[b]), int(case.context_lens[b])
+        first = n - ql + 1  # keys seen by the first query row
+        pairs += ql * first + ql * (ql - 1) // 2
+    return 4 * case.head_dim * case.num_q_heads * pairs
+
+
+def time_prefill(case: wl.PagedCase, steps: int, warmup: int):
+    """Times store (all prompt tokens) + prefill; returns (store_ms, prefill_ms)."""
+    dev = place(case)
+    out = torch.empty((case.total_q_rows, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache,
+                   dev.v_cache, dev.block_table, case.scale)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    sto = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    pre = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    del dev
+    torch.cuda.empty_cache()
+    return sto, pre
+
+
+def prefill_report(steps: int, warmup: int) -> dict:
+    c = wl.prefill_8x2048()
+    sto, pre = time_prefill(c, steps, warmup)
+    fl = prefill_flops(c)
+    sb = store_bytes(c.total_kv_rows, c.num_kv_heads)
+    tf = fl / (pre * 1e-3) / 1e12
+    return {"workload": c.name, "prefill_ms": round(pre, 4), "causal_gflop": round(fl / 1e9, 3),
+            "prefill_TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "store_ms": round(sto, 4), "store_tokens": c.total_kv_rows,
+            "store_GBps": round(sb / (sto * 1e-3) / 1e9, 1),
+            "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
     """The oracle as it stands, timed on the host cores on a bounded sample of
     the same workload: whole sequences in batch order (wrapping around to the
@@ -134,6 +190,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="qwen3_0.6b_decode", choices=sorted(wl.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time store + prefill of the 8 x 2048 prompt batch (for profiling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -145,6 +203,10 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
     pa.lib()
+
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_report(args.steps, args.warmup)}), flush=True)
+        return 0
 
     case = wl.CONFIGS[args.workload]()
     if case.kind != "decode":
@@ -196,6 +258,8 @@ def main(argv=None):
                            "frac_of_hbm_peak": round(b / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "attended_tokens_per_s": round(int(c.context_lens.sum()) / (d * 1e-3), 1),
                            "sum_context_len": int(c.context_lens.sum())}
+        print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
+        extra["prefill_8x2048"] = prefill_report(max(10, args.steps // 5), 3)
         line["extra"] = extra
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

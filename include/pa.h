@@ -140,8 +140,12 @@ size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_
  *                   (must be <= max_blocks_per_seq*block_size).
  *   scale         : the logit scale (e.g. 1/sqrt(head_dim)); finite.
  *   workspace     : >= pa_decode_workspace_size(...) bytes of device memory,
- *                   256-B aligned; its contents need no initialisation and are
- *                   scratch after the call returns.
+ *                   256-B aligned.  It must be ZERO-FILLED before its first
+ *                   use; every call leaves it zero-filled again (it holds one
+ *                   arrival counter per (sequence, kv head) that the last
+ *                   contributing wave resets, plus partial results that are
+ *                   scratch).  Calls that overlap in time must not share a
+ *                   workspace.
  *   Source: CSDN essay, first and third sections; vLLM decode kernel
  *   description in the same essay.
  */

@@ -154,8 +154,10 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int) -> in
 
 
 def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, device="cuda"):
+    """A zero-filled decode workspace (pa_decode leaves it zero-filled, so it
+    can be reused by later calls of the same or a smaller shape)."""
     n = decode_workspace_size(batch, num_q_heads, num_kv_heads)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_len: int,

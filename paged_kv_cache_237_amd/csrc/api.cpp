@@ -83,10 +83,17 @@ int64_t decode_waves(int cus, int32_t batch, int32_t num_kv_heads, int32_t max_c
   return std::max<int64_t>(1, std::min(w, tiles_upper));
 }
 
+// Workspace: one int arrival counter per (sequence, kv head) segment, padded
+// to 256 bytes, then the partial records (batch*Hkv + waves of them).
+size_t decode_counter_bytes(int32_t batch, int32_t num_kv_heads) {
+  const size_t bytes = size_t(int64_t(batch) * num_kv_heads) * sizeof(int);
+  return (bytes + 255) & ~size_t(255);
+}
+
 size_t decode_ws_bytes(int32_t batch, int32_t num_kv_heads, int group, int64_t waves) {
   const int64_t records = int64_t(batch) * num_kv_heads + waves;
   const size_t bytes = size_t(records) * size_t(pa::partial_floats(group)) * sizeof(float);
-  return (bytes + 255) & ~size_t(255);
+  return decode_counter_bytes(batch, num_kv_heads) + ((bytes + 255) & ~size_t(255));
 }
 
 }  // namespace
@@ -219,7 +226,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len);
     const size_t need = decode_ws_bytes(batch, num_kv_heads, group, waves);
     if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
-    if (!aligned(workspace, 16)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
                                         std::to_string(workspace_bytes));
@@ -230,7 +237,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.block_table = block_table;
     a.ctx_lens = context_lens;
     a.out = static_cast<uint16_t*>(out);
-    a.ws = static_cast<float*>(workspace);
+    a.counters = static_cast<int*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    decode_counter_bytes(batch, num_kv_heads));
     a.num_blocks = num_blocks;
     a.batch = batch;
     a.hkv = num_kv_heads;

@@ -10,10 +10,13 @@
 // ceil(ctx/64) tiles of 64 tokens.  All segments are laid end to end and the
 // resulting list of tiles is cut into n_waves equal runs, one per wave, so
 // every wave streams the same number of bytes whatever the length mix.  A run
-// that covers a whole segment writes the bf16 output at once; a segment cut
-// between runs leaves one partial state (m, l, u) per run in the workspace,
-// and a second kernel merges those:  M = max m_i,  L = sum 2^(m_i-M) l_i,
-// o = sum 2^(m_i-M) u_i / L  (the split-context form of the online softmax).
+// that covers a whole segment writes the bf16 output at once.  A segment cut
+// between runs leaves one partial state (m, l, u) per run in the workspace;
+// each contributing wave then bumps the segment's counter (agent-scope
+// atomic after a release fence) and the last one to arrive merges them:
+// M = max m_i,  L = sum 2^(m_i-M) l_i,  o = sum 2^(m_i-M) u_i / L  (the
+// split-context form of the online softmax), and resets the counter to zero,
+// so the workspace counters are zero again after every call.
 // The partial of segment s written by wave w goes to record s + w: segments
 // and runs are both contiguous intervals of the tile list, so two distinct
 // non-empty (segment, run) intersections never share s + w.
@@ -59,18 +62,6 @@ __device__ int total_tiles(const DecodeArgs& a) {
   return tot * a.hkv;
 }
 
-// Tiles of the sequences before b (identical in every lane).
-__device__ int tiles_before(const DecodeArgs& a, int b) {
-  const int lane = lane_id();
-  int tot = 0;
-  for (int b0 = 0; b0 < b; b0 += kWave) {
-    const int bb = b0 + lane;
-    const int nt = bb < b ? tiles_of(clamp_ctx(a, a.ctx_lens[bb])) : 0;
-    tot += wave_sum_i(nt);
-  }
-  return tot;
-}
-
 // Sequence holding tile `pos` of the flattened list and the tiles of all
 // sequences before it.
 __device__ void locate(const DecodeArgs& a, int pos, int& b_out, int& before_out) {
@@ -92,6 +83,66 @@ __device__ void locate(const DecodeArgs& a, int pos, int& b_out, int& before_out
   }
   b_out = a.batch;
   before_out = base;
+}
+
+// Partial records cross XCDs (each XCD has its own L2), so they are written
+// and read with agent-scope atomic accesses, which the hardware keeps coherent
+// by themselves (no whole-L2 writeback or invalidate is needed, unlike a
+// device-scope fence).
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the partial records of segment `seg` written by waves w0..w1 into
+// its G output rows (lane = 2 dims).  One pass with an online rescale; the
+// loads of four records are issued together.
+template <int G>
+__device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0, int w1) {
+  const int lane = lane_id();
+  const int hq = a.hkv * G;
+  float M[G], L[G], U0[G], U1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    M[h] = -INFINITY;
+    L[h] = U0[h] = U1[h] = 0.f;
+  }
+  for (int w = w0; w <= w1; w += 4) {
+    float mm[4][G], ll[4][G], ua[4][G], ub[4][G];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool have = w + j <= w1;
+      const float* rec = a.ws + int64_t(seg + (have ? w + j : w0)) * partial_floats(G);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        mm[j][h] = have ? ld_coherent(rec + G * kDim + h) : -INFINITY;
+        ll[j][h] = have ? ld_coherent(rec + G * kDim + G + h) : 0.f;
+        ua[j][h] = have ? ld_coherent(rec + h * kDim + 2 * lane) : 0.f;
+        ub[j][h] = have ? ld_coherent(rec + h * kDim + 2 * lane + 1) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(M[h], mm[j][h]);
+        const float ref = mn == -INFINITY ? 0.f : mn;
+        const float sa = __builtin_amdgcn_exp2f(M[h] - ref);
+        const float sb = __builtin_amdgcn_exp2f(mm[j][h] - ref);
+        L[h] = L[h] * sa + ll[j][h] * sb;
+        U0[h] = U0[h] * sa + ua[j][h] * sb;
+        U1[h] = U1[h] * sa + ub[j][h] * sb;
+        M[h] = mn;
+      }
+  }
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.out + (int64_t(b) * hq + g * G) * kDim);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float inv = L[h] > 0.f ? 1.f / L[h] : 0.f;
+    out[h * (kDim / 2) + lane] = pack_bf16x2(U0[h] * inv, U1[h] * inv);
+  }
 }
 
 template <int G>
@@ -226,22 +277,21 @@ __device__ void decode_run(const DecodeArgs& a, int b, int g, int t_lo, int t_hi
       }
     }
   } else {
-    float* rec = a.ws + int64_t(b * a.hkv + g + wave) * partial_floats(G);
+    const int seg = b * a.hkv + g;
+    float* rec = a.ws + int64_t(seg + wave) * partial_floats(G);
     if (lane < 16) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float4* dst = reinterpret_cast<float4*>(rec + h * kDim + lane * 8);
-        dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-        dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-      }
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st_coherent(rec + h * kDim + lane * 8 + e, acc[h][e]);
     }
     if (lane < G) {
       float mv = m[0], lv = l[0];
 #pragma unroll
       for (int h = 1; h < G; ++h)
         if (lane == h) { mv = m[h]; lv = l[h]; }
-      rec[G * kDim + lane] = mv;
-      rec[G * kDim + G + lane] = lv;
+      st_coherent(rec + G * kDim + lane, mv);
+      st_coherent(rec + G * kDim + G + lane, lv);
     }
   }
 }
@@ -252,6 +302,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float p_lds[kWavesPerWG][kTile * G];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave = blockIdx.x * kWavesPerWG + wv;
+
+  // Empty contexts have no tiles: their output rows are zero.
+  if (wave < a.n_waves) {
+    const int hq = a.hkv * G;
+    for (int bb = wave; bb < a.batch; bb += a.n_waves) {
+      if (clamp_ctx(a, a.ctx_lens[bb]) != 0) continue;
+      uint32_t* o = reinterpret_cast<uint32_t*>(a.out + int64_t(bb) * hq * kDim);
+      for (int i = lane_id(); i < hq * (kDim / 2); i += kWave) o[i] = 0u;
+    }
+  }
 
   const int total = total_tiles(a);
   const int per = (total + a.n_waves - 1) / a.n_waves;
@@ -266,9 +326,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   int off = pos - before * a.hkv;
   int g = off / nt;
   int t = off - g * nt;
+  // A run cuts at most two segments (its first and its last); their arrivals
+  // are counted once the whole run has been streamed, so the record stores
+  // never stall the loads.
+  int pend_b[2], pend_g[2], pend_w0[2], pend_w1[2];
+  int npend = 0;
   while (true) {
     const int take = min(nt - t, end - pos);
     decode_run<G>(a, b, g, t, t + take, nt, wave, q_lds[wv], p_lds[wv]);
+    if (!(t == 0 && take == nt)) {
+      const int start = pos - t;  // first tile of the segment in the flattened list
+      pend_b[npend] = b;
+      pend_g[npend] = g;
+      pend_w0[npend] = start / per;
+      pend_w1[npend] = (start + nt - 1) / per;
+      ++npend;
+    }
     pos += take;
     if (pos >= end) break;
     t = 0;
@@ -281,50 +354,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       if (b >= a.batch) break;
     }
   }
-}
 
-// One wave per segment: merge its partial states, or write zeros for an empty
-// context.  Segments finished by a single run were written by the split kernel.
-template <int G>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  const int lane = lane_id();
-  const int seg = blockIdx.x * kWavesPerWG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (seg >= a.batch * a.hkv) return;
-  const int b = seg / a.hkv;
-  const int g = seg - b * a.hkv;
-  const int hq = a.hkv * G;
-  const int nt = tiles_of(clamp_ctx(a, a.ctx_lens[b]));
-  uint32_t* out = reinterpret_cast<uint32_t*>(a.out + (int64_t(b) * hq + g * G) * kDim);
-  if (nt == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) out[h * (kDim / 2) + lane] = 0u;
-    return;
-  }
-  const int total = total_tiles(a);
-  const int per = (total + a.n_waves - 1) / a.n_waves;
-  const int start = tiles_before(a, b) * a.hkv + g * nt;
-  const int w0 = start / per;
-  const int w1 = (start + nt - 1) / per;
-  if (w0 == w1) return;
-
-  for (int h = 0; h < G; ++h) {
-    float big = -INFINITY;
-    for (int w = w0; w <= w1; ++w) {
-      const float* rec = a.ws + int64_t(seg + w) * partial_floats(G);
-      big = fmaxf(big, rec[G * kDim + h]);
+  if (npend > 0) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's record stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    for (int i = 0; i < npend; ++i) {
+      const int seg = pend_b[i] * a.hkv + pend_g[i];
+      int prev = 0;
+      if (lane_id() == 0)
+        prev = __hip_atomic_fetch_add(a.counters + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev == pend_w1[i] - pend_w0[i]) {
+        merge_segment<G>(a, seg, pend_b[i], pend_g[i], pend_w0[i], pend_w1[i]);
+        if (lane_id() == 0)
+          __hip_atomic_store(a.counters + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    const float ref = big == -INFINITY ? 0.f : big;
-    float sum = 0.f, u0 = 0.f, u1 = 0.f;
-    for (int w = w0; w <= w1; ++w) {
-      const float* rec = a.ws + int64_t(seg + w) * partial_floats(G);
-      const float f = __builtin_amdgcn_exp2f(rec[G * kDim + h] - ref);
-      sum = fmaf(f, rec[G * kDim + G + h], sum);
-      const float2 u = reinterpret_cast<const float2*>(rec + h * kDim)[lane];
-      u0 = fmaf(f, u.x, u0);
-      u1 = fmaf(f, u.y, u1);
-    }
-    const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    out[h * (kDim / 2) + lane] = pack_bf16x2(u0 * inv, u1 * inv);
   }
 }
 
@@ -332,10 +378,6 @@ template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
   const unsigned split_blocks = unsigned((a.n_waves + kWavesPerWG - 1) / kWavesPerWG);
   hipLaunchKernelGGL(decode_split_kernel<G>, dim3(split_blocks), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned merge_blocks = unsigned((a.batch * a.hkv + kWavesPerWG - 1) / kWavesPerWG);
-  hipLaunchKernelGGL(decode_merge_kernel<G>, dim3(merge_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -36,7 +36,8 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   uint16_t* out;
-  float* ws;
+  float* ws;         // partial records (after the counters)
+  int* counters;     // one arrival counter per segment; zero between calls
   int64_t num_blocks;
   int batch;
   int hkv;
