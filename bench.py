@@ -55,6 +55,18 @@ def place(case):
     return _place(case)
 
 
+def copy_probe(mib: int) -> None:
+    """One plain device-to-device copy of `mib` MiB (outside any timing)."""
+    if mib <= 0:
+        return
+    src = torch.ones(mib * 2**20 // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def time_decode(case: wl.PagedCase, steps: int, warmup: int):
     """Times `steps` decode steps (store + decode) after `warmup`; returns
     (ms_per_step, decode_ms_avg, store_ms_avg)."""
@@ -147,6 +159,115 @@ def prefill_report(steps: int, warmup: int) -> dict:
             "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+# ---------------------------------------------------------------------------
+# Profile summaries (rocprofv3 CSV -> short text/JSON under profiles/)
+
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", "decode.hip")
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _read_csv(path: str):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
+    """Kernel-trace statistics of a rocprofv3 run, as a short Markdown table."""
+    rows = _read_csv(stats_csv)
+    lines = ["# rocprofv3 kernel statistics", "", "Command (run from the repository root):", "",
+             "```", command, "```", "",
+             "Library kernels and device copies only; the other kernels of the run are torch "
+             "kernels that generate the seeded inputs before timing.", "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        if "pa::" not in r["Name"] and "copyBuffer" not in r["Name"]:
+            continue
+        name = r["Name"]
+        short = name if len(name) < 70 else name[:67] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def _pmc_per_kernel(counter_csv: str, counter: str):
+    """Values of `counter` per dispatch, per kernel name."""
+    acc = {}
+    for r in _read_csv(counter_csv):
+        if r.get("Counter_Name") != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key: str,
+                      out_json: str, commands) -> dict:
+    """HBM bytes per launch of the kernel whose name contains kernel_key, from
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the value the
+    same counter reads for a plain device copy of copy_mib MiB."""
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        """Average over the dispatches of the kernel matching key."""
+        hits = [(k, v) for k, v in d.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}: {sorted(d)}")
+        k, v = max(hits, key=lambda kv: len(kv[1]))
+        return k, (sum(v) / len(v), len(v))
+
+    def pick_copy(d):
+        """The single largest copy dispatch: the copy of known size."""
+        best = None
+        for k, v in d.items():
+            if "copyBuffer" in k or "elementwise_kernel" in k:
+                m = max(v)
+                if best is None or m > best[1][0]:
+                    best = (k, (m, 1))
+        if best is None:
+            raise SystemExit("no copy kernel in the counter CSV")
+        return best
+
+    known = copy_mib * 2**20
+    kf, (kfv, kfn) = pick(fetch, kernel_key)
+    kw, (kwv, kwn) = pick(write, kernel_key)
+    cf, (cfv, _) = pick_copy(fetch)
+    cw, (cwv, _) = pick_copy(write)
+    f_scale = known / (cfv * 1024.0)
+    w_scale = known / (cwv * 1024.0)
+    res = {
+        "kernel": kf, "dispatches": int(kfn),
+        "fetch_kib_raw": kfv, "write_kib_raw": kwv,
+        "copy_kernel": cf, "copy_bytes": known,
+        "copy_fetch_kib_raw": cfv, "copy_write_kib_raw": cwv,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "fetch_bytes": kfv * 1024.0 * f_scale, "write_bytes": kwv * 1024.0 * w_scale,
+        "traffic_bytes": kfv * 1024.0 * f_scale + kwv * 1024.0 * w_scale,
+        "decode_source_sha256_16": source_digest(DECODE_SRC),
+        "commands": list(commands),
+    }
+    json.dump(res, open(out_json, "w"), indent=1)
+    return res
+
+
+def recorded_traffic(workload: str):
+    """Traffic per launch from the committed counter summary of this workload,
+    if the decode kernel source has not changed since it was taken."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("decode_source_sha256_16") != source_digest(DECODE_SRC):
+        return None
+    return int(round(rec["traffic_bytes"]))
+
+
 def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
     """The oracle as it stands, timed on the host cores on a bounded sample of
     the same workload: whole sequences in batch order (wrapping around to the
@@ -192,7 +313,25 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="skip the other workload shapes")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time store + prefill of the 8 x 2048 prompt batch (for profiling)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
+                    help="write a Markdown summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-traffic", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB", "KERNEL_KEY", "OUT_JSON"),
+                    help="write the per-launch HBM traffic of a kernel from FETCH_SIZE / "
+                         "WRITE_SIZE counter CSVs and exit")
+    ap.add_argument("--commands", nargs="*", default=[],
+                    help="the profiler commands recorded in a traffic summary")
     args = ap.parse_args(argv)
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return 0
+    if args.summarize_traffic:
+        f, w, mib, key, out = args.summarize_traffic
+        print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands)))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               f"(the path is single-GPU; sharding is described in the design notes)",
@@ -206,6 +345,7 @@ def main(argv=None):
 
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_report(args.steps, args.warmup)}), flush=True)
+        copy_probe(args.copy_probe_mib)
         return 0
 
     case = wl.CONFIGS[args.workload]()
@@ -215,6 +355,7 @@ def main(argv=None):
     print(f"[bench] {case.name}: B={case.batch} sum_ctx={int(case.context_lens.sum())}",
           file=sys.stderr, flush=True)
     ms_step, dec_ms, sto_ms = time_decode(case, args.steps, args.warmup)
+    copy_probe(args.copy_probe_mib)
     dbytes = decode_bytes(case)
     sbytes = store_bytes(case.batch, case.num_kv_heads)
     sum_ctx = int(case.context_lens.sum())
@@ -244,7 +385,7 @@ def main(argv=None):
         "store_ms": round(sto_ms, 4),
         "roofline": {"bound": "hbm", "kernel": "pa_decode (split-context pass + merge pass)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(case.name),
                      "algorithmic_bytes_per_launch": dbytes},
     }
     if not args.no_extra:
