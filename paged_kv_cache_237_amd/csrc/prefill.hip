@@ -37,25 +37,104 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kRowsPerWG = 128;  // query rows (head, position) per workgroup
+constexpr int kRowsPerWG = 128;  // query rows (head, position) per workgroup: 32 per wave
 constexpr int kKeys = 64;        // keys per K/V tile
 constexpr int kVtStride = 68;    // bf16 per transposed-V row in LDS (64 keys + pad)
 constexpr float kLazyRescale = 8.f;  // log2 headroom before O is rescaled
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
-struct __align__(16) PrefillSmem {
-  uint4 k[kChunks * kKeys];              // [chunk][key] 16-byte chunks: 16 KiB
-  uint16_t vt[kDim * kVtStride];         // [dim][key] bf16: 17 KiB
-  float rowf[4][32];                     // per-wave row factors
+// LDS: two K tiles and two transposed V tiles; tile t is read from buffer t&1
+// while tile t+1 waits in registers.
+struct __align__(16) PrefillLds {
+  uint4 k[2][kChunks * kKeys];        // [buf][chunk][key] 16-byte chunks: 2 x 16 KiB
+  uint16_t vt[2][kDim * kVtStride];   // [buf][dim][key] bf16: 2 x 17 KiB
+  float rowf[4][32];                  // per-wave row factors
 };
+constexpr size_t kPrefillLds = sizeof(PrefillLds);
+static_assert(sizeof(PrefillLds) >= 4 * 32 * kDim * 2, "epilogue staging fits");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
+struct TileGeom {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int r0, valid;
+};
+
+__device__ __forceinline__ TileGeom tile_geom(const PrefillArgs& a, const int32_t* table, int g,
+                                              int ctx, int t) {
+  const int key0 = t * kKeys;
+  const int phys = table[key0 / kBlock];
+  const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
+  TileGeom tg;
+  tg.valid = ok ? min(kKeys, ctx - key0) : 0;
+  tg.r0 = key0 % kBlock;
+  const int64_t bh = (ok ? int64_t(phys) : 0) * a.hkv + g;
+  tg.rk = make_rsrc(a.k_cache + bh * (kChunks * kBlock), 65536u);
+  // keys past the context load zeros (the cache may hold NaN patterns there)
+  tg.rv = make_rsrc(a.v_cache + bh * (kBlock * kChunks), uint32_t(tg.r0 + tg.valid) * 256u);
+  return tg;
+}
+
+// K tile t -> registers: 4 chunks per thread.
+__device__ __forceinline__ void load_k(const PrefillArgs& a, const int32_t* table, int g, int ctx,
+                                       int t, int tid, uint4 (&kx)[4]) {
+  const TileGeom tg = tile_geom(a, table, g, ctx, t);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + 256 * j;
+    const int ch = i >> 6, row = i & 63;
+    const uint32_t off = row < tg.valid ? uint32_t(ch * kBlock + tg.r0 + row) * 16u : kOutOfRange;
+    kx[j] = buf_load16(tg.rk, off, 0u);
+  }
+}
+
+// V tile t -> registers: 2 chunks of 2 consecutive keys per thread.
+__device__ __forceinline__ void load_v(const PrefillArgs& a, const int32_t* table, int g, int ctx,
+                                       int t, int tid, uint4 (&va)[2], uint4 (&vb)[2]) {
+  const TileGeom tg = tile_geom(a, table, g, ctx, t);
+  const int kp = tid & 31;  // key pair
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ch = (tid >> 5) + 8 * j;
+    const uint32_t off = uint32_t((tg.r0 + 2 * kp) * kChunks + ch) * 16u;
+    va[j] = buf_load16(tg.rv, off, 0u);
+    vb[j] = buf_load16(tg.rv, off + 256u, 0u);
+  }
+}
+
+__device__ __forceinline__ void store_k(uint4* kbuf, int tid, const uint4 (&kx)[4]) {
+  uint4* kdst = kbuf + tid;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kdst[256 * j] = kx[j];
+}
+
+// V transposed to [dim][key], pairs of keys per dword; every address is a
+// per-thread base plus a compile-time offset.
+__device__ __forceinline__ void store_v(uint16_t* vtbuf, int tid, const uint4 (&va)[2],
+                                        const uint4 (&vb)[2]) {
+  // thread (kp = tid%32, ch = tid/32 (+8)): dims 8*ch .. 8*ch+7, keys 2kp, 2kp+1
+  uint32_t* vdst = reinterpret_cast<uint32_t*>(vtbuf) + ((tid >> 5) * 8 * kVtStride) / 2 + (tid & 31);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t r0w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+    const uint32_t r1w[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 64 * j + 2 * e;  // dim offset from this thread's first dim
+      vdst[(d * kVtStride) / 2] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x05040100u);
+      vdst[((d + 1) * kVtStride) / 2] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x07060302u);
+    }
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int QB = kRowsPerWG / G;  // positions per workgroup
-  __shared__ PrefillSmem sm;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  PrefillLds& sm = *reinterpret_cast<PrefillLds*>(lds_raw);
+  float (*rowf)[32] = sm.rowf;
 
   const int b = blockIdx.x;
   const int g = blockIdx.y;
@@ -93,6 +172,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   amax = __builtin_amdgcn_readfirstlane(amax);
   amin = __builtin_amdgcn_readfirstlane(amin);
 
+  // Keys the whole workgroup needs.
+  const int last_row = min(p0 + QB, qlen) - 1;
+  const int kend = min(shift + last_row + 1, ctx);
+  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+  const int32_t* table = a.block_table + int64_t(b) * a.mbps;
+
   // Q^T operand: dims 16*ks + 8*half .. +7 of the lane's row, 8 k-steps.
   bf16x8_t qop[8];
   {
@@ -102,10 +187,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(row_ok ? qrow[2 * ks + half] : zero4());
   }
 
-  // Keys the whole workgroup needs.
-  const int last_row = min(p0 + QB, qlen) - 1;
-  const int kend = min(shift + last_row + 1, ctx);
-  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+  // Tile t+1 is loaded into registers while tile t is computed from LDS;
+  // the two LDS buffers alternate.
+  uint4 kx[4], va[2], vb[2];
+  if (ntiles > 0) {
+    load_k(a, table, g, ctx, 0, tid, kx);
+    load_v(a, table, g, ctx, 0, tid, va, vb);
+  }
 
   const float c = a.scale_log2;
   f32x16_t o[4];
@@ -116,73 +204,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY;  // running reference max of the lane's row (log2 units)
   float l = 0.f;        // partial row sum over this lane's keys
 
-  const int32_t* table = a.block_table + int64_t(b) * a.mbps;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int key0 = t * kKeys;
-    const int phys = table[key0 / kBlock];
-    const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
-    const int valid = ok ? min(kKeys, ctx - key0) : 0;
-    const int r0 = key0 % kBlock;
-    const int64_t bh = (ok ? int64_t(phys) : 0) * a.hkv + g;
-
-    // ---- stage K (as is) and V (transposed) of this tile in LDS ----------
-    {
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + bh * (kChunks * kBlock), 65536u);
-      const __amdgpu_buffer_rsrc_t rv =
-          make_rsrc(a.v_cache + bh * (kBlock * kChunks), uint32_t(r0 + valid) * 256u);
-      uint4 kx[4];
+  // S^T = K Q^T of tile t from K buffer t&1: two independent 32-key chains.
+  auto scores = [&](int t, f32x16_t (&s)[2]) {
+    const uint4* ksrc = sm.k[t & 1] + half * kKeys + col;  // chunk 2ks+half, key 32ms+col
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = tid + 256 * j;
-        const int ch = i >> 6, row = i & 63;
-        const uint32_t off = row < valid ? uint32_t(ch * kBlock + r0 + row) * 16u : kOutOfRange;
-        kx[j] = buf_load16(rk, off, 0u);
-      }
-      const int kp = tid & 31;  // key pair
-      uint4 va[2], vb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ch = (tid >> 5) + 8 * j;
-        const uint32_t off = uint32_t((r0 + 2 * kp) * kChunks + ch) * 16u;
-        va[j] = buf_load16(rv, off, 0u);
-        vb[j] = buf_load16(rv, off + 256u, 0u);
-      }
-      __syncthreads();  // previous tile fully consumed
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sm.k[tid + 256 * j] = kx[j];
-      uint32_t* vt32 = reinterpret_cast<uint32_t*>(sm.vt);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ch = (tid >> 5) + 8 * j;
-        const uint32_t r0w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
-        const uint32_t r1w[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = ch * 8 + 2 * e;
-          vt32[(d * kVtStride) / 2 + kp] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x05040100u);
-          vt32[((d + 1) * kVtStride) / 2 + kp] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x07060302u);
-        }
-      }
-      __syncthreads();
-    }
-
-    if (key0 > amax) continue;  // every key of the tile is above this wave's diagonal
-
-    // ---- S^T = K Q^T : two 32-key subtiles --------------------------------
-    f32x16_t s[2];
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
+    for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[ms][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t ka = as_bf16x8(sm.k[(2 * ks + half) * kKeys + 32 * ms + col]);
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) {
+        const bf16x8_t ka = as_bf16x8(ksrc[2 * ks * kKeys + 32 * ms]);
         s[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], s[ms], 0, 0, 0);
       }
     }
+  };
 
-    // ---- mask keys past the row's position (diagonal / tail tiles) -------
+  // Softmax of tile t's scores and O += P V with V buffer t&1.
+  auto softmax_pv = [&](int t, f32x16_t (&s)[2]) {
+    const int key0 = t * kKeys;
+    // mask keys past the row's position (diagonal / tail tiles)
     if (key0 + kKeys - 1 > amin) {
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms)
@@ -192,8 +234,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
           s[ms][r] = key <= a_pos ? s[ms][r] : -INFINITY;
         }
     }
-
-    // ---- online softmax with lazy rescale ---------------------------------
+    // online softmax with lazy rescale
     float mt = -INFINITY;
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms)
@@ -208,11 +249,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         l *= alpha;
         m = mnew;
       }
-      if (half == 0) sm.rowf[w][col] = alpha;
+      if (half == 0) rowf[w][col] = alpha;
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const float4 al = *reinterpret_cast<const float4*>(&sm.rowf[w][8 * qd + 4 * half]);
+        const float4 al = *reinterpret_cast<const float4*>(&rowf[w][8 * qd + 4 * half]);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           o[n][4 * qd + 0] *= al.x;
@@ -225,10 +266,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
     const float mref = m == -INFINITY ? 0.f : m;
 
-    // ---- P = 2^(c s - m) as bf16 A operands, row sums --------------------
-    // The row sum adds the bf16-rounded weights the MFMA actually uses, so
-    // the output is a convex combination of V rows with consistently rounded
-    // weights (a dominant weight cancels exactly in O / l).
+    // P = 2^(c s - m) as bf16 A operands; row sums of the rounded weights
     bf16x8_t pop[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -237,36 +275,55 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 8; ++e)
         pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][8 * (ks & 1) + e], c, -mref));
       const uint4 pb = pack8(pf);
-      l += (bf16_lo(pb.x) + bf16_hi(pb.x)) + (bf16_lo(pb.y) + bf16_hi(pb.y)) +
-           (bf16_lo(pb.z) + bf16_hi(pb.z)) + (bf16_lo(pb.w) + bf16_hi(pb.w));
+      // sum of the bf16 weights the MFMA consumes (dot with (1, 1) pairs)
+      l = dot2_bf16(pb.x, kBf16OnePair, l);
+      l = dot2_bf16(pb.y, kBf16OnePair, l);
+      l = dot2_bf16(pb.z, kBf16OnePair, l);
+      l = dot2_bf16(pb.w, kBf16OnePair, l);
       pop[ks] = as_bf16x8(pb);
     }
 
-    // ---- O += P V ------------------------------------------------------------
-    const uint32_t* vt32 = reinterpret_cast<const uint32_t*>(sm.vt);
+    // O += P V; lane reads dims 32n + col, keys 16ks + 4*half + {0..3, 8..11}
+    const uint32_t* vsrc =
+        reinterpret_cast<const uint32_t*>(sm.vt[t & 1]) + (col * kVtStride + 4 * half) / 2;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int dim = 32 * n + col;
-        const int base = (dim * kVtStride + 16 * ks + 4 * half) / 2;  // in dwords
-        const uint2 lo = *reinterpret_cast<const uint2*>(vt32 + base);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vt32 + base + 4);
+        const int off = (32 * n * kVtStride + 16 * ks) / 2;  // in dwords, compile-time
+        const uint2 lo = *reinterpret_cast<const uint2*>(vsrc + off);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vsrc + off + 4);
         const bf16x8_t vop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], vop, o[n], 0, 0, 0);
       }
     }
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    // Buffer t&1 last held tile t-2, which every wave finished computing
+    // before the previous barrier.
+    store_k(sm.k[t & 1], tid, kx);
+    store_v(sm.vt[t & 1], tid, va, vb);
+    if (t + 1 < ntiles) {
+      load_k(a, table, g, ctx, t + 1, tid, kx);
+      load_v(a, table, g, ctx, t + 1, tid, va, vb);
+    }
+    __syncthreads();
+    if (t * kKeys > amax) continue;  // every key of the tile is above this wave's diagonal
+    f32x16_t s[2];
+    scores(t, s);
+    softmax_pv(t, s);
   }
 
   // ---- epilogue: O / l -> bf16, staged through LDS for 16-byte stores -------
-  __syncthreads();  // K/V buffers are reused below
+  __syncthreads();  // tile buffers are reused below
   const float ltot = l + __shfl_xor(l, 32, 64);
-  if (half == 0) sm.rowf[w][col] = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (half == 0) rowf[w][col] = ltot > 0.f ? 1.f / ltot : 0.f;
   __builtin_amdgcn_wave_barrier();
-  uint16_t* stage = reinterpret_cast<uint16_t*>(sm.k) + w * (32 * kDim);  // [32 rows][128]
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds_raw) + w * (32 * kDim);  // [32 rows][128]
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
-    const float4 inv = *reinterpret_cast<const float4*>(&sm.rowf[w][8 * qd + 4 * half]);
+    const float4 inv = *reinterpret_cast<const float4*>(&rowf[w][8 * qd + 4 * half]);
     const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -299,9 +356,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
   constexpr int QB = kRowsPerWG / G;
+  // more than 64 KiB of LDS per workgroup must be opted into
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&prefill_kernel<G>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(kPrefillLds));
+  if (attr != hipSuccess) return attr;
   const int nqb = (a.max_q + QB - 1) / QB;
   const dim3 grid(unsigned(a.batch), unsigned(a.hkv), unsigned(nqb));
-  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), kPrefillLds, s, a);
   return hipGetLastError();
 }
 
