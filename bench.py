@@ -67,16 +67,22 @@ def copy_probe(mib: int) -> None:
     del src, dst
 
 
-def time_decode(case: wl.PagedCase, steps: int, warmup: int):
-    """Times `steps` decode steps (store + decode) after `warmup`; returns
-    (ms_per_step, decode_ms_avg, store_ms_avg)."""
+def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True):
+    """Times `steps` decode steps (store of the new tokens + decode) after
+    `warmup`; returns (ms_per_step, decode_ms_avg, store_ms_avg).
+
+    ms_per_step: the step captured once in a HIP graph and replayed `steps`
+    times (a serving loop replays its step; this removes host launch gaps),
+    or eager launches with graph=False.  decode_ms / store_ms: HIP events
+    around each call in a separate eager loop, on the stream the kernels run
+    on."""
     dev = place(case)
     out = torch.empty((case.batch, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
                       device="cuda")
     ws = pa.alloc_decode_workspace(case.batch, case.num_q_heads, case.num_kv_heads)
-    stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        stream = torch.cuda.current_stream()
         if ev is not None:
             ev[0].record(stream)
         pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
@@ -89,15 +95,37 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int):
 
     for _ in range(warmup):
         step()
+    # per-kernel events (eager)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     dec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     sto = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    # whole steps
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        run = g.replay
+    else:
+        run = step
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     del dev
     torch.cuda.empty_cache()
     return wall * 1e3 / steps, dec, sto
@@ -311,6 +339,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="qwen3_0.6b_decode", choices=sorted(wl.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replaying the step as a HIP graph")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time store + prefill of the 8 x 2048 prompt batch (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -354,7 +384,7 @@ def main(argv=None):
         return 2
     print(f"[bench] {case.name}: B={case.batch} sum_ctx={int(case.context_lens.sum())}",
           file=sys.stderr, flush=True)
-    ms_step, dec_ms, sto_ms = time_decode(case, args.steps, args.warmup)
+    ms_step, dec_ms, sto_ms = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
     copy_probe(args.copy_probe_mib)
     dbytes = decode_bytes(case)
     sbytes = store_bytes(case.batch, case.num_kv_heads)
@@ -381,9 +411,10 @@ def main(argv=None):
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "attended_tokens_per_s": round(sum_ctx / (ms_step * 1e-3), 1),
+        "step_launch": "hip graph replay" if not args.no_graph else "eager",
         "decode_ms": round(dec_ms, 4),
         "store_ms": round(sto_ms, 4),
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (split-context pass + merge pass)",
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (pa_decode: split-context streaming with fused merge)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(case.name),
                      "algorithmic_bytes_per_launch": dbytes},

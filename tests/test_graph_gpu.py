@@ -1,0 +1,58 @@
+"""The decode step (pa_store_kv then pa_decode) captured in a HIP graph and
+replayed: every replay must give the same bits as the eager calls, also with
+other eager work and synchronisations between replays.  The library's
+kernels use no memset nodes; the decode workspace counters are reset by the
+kernel itself, so replays need no re-initialisation."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_237_amd as pa
+import workloads as wl
+from paged_harness import bf16_out_to_f64, compare, oracle_pools, place
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_0.6b_decode"])
+def test_graph_replays_match_eager(name):
+    case = wl.CONFIGS[name]()
+    print(f"[graph] {case.name}", flush=True)
+    dev = place(case)
+    out = torch.zeros((case.batch, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    ws = pa.alloc_decode_workspace(case.batch, case.num_q_heads, case.num_kv_heads)
+
+    def step():
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        pa.decode(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens,
+                  case.max_context_len, case.scale, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.synchronize()
+
+    for i in range(4):
+        out.zero_()
+        scratch = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        del scratch
+
+    kp, vp = oracle_pools(case)
+    ref = oracle.decode(wl.bits_to_numpy(case.q_all()), kp, vp, case.block_table,
+                        case.context_lens, case.scale)
+    compare(bf16_out_to_f64(out), ref, f"{name} graph")
