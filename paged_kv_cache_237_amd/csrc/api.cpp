@@ -76,10 +76,11 @@ int check_geometry(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
   return PA_OK;
 }
 
-int64_t decode_waves(int cus, int32_t batch, int32_t num_kv_heads, int32_t max_context_len) {
+int64_t decode_waves(int cus, int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int group) {
   const int64_t tiles_upper =
       int64_t(batch) * num_kv_heads * ((int64_t(max_context_len) + pa::kTile - 1) / pa::kTile);
-  const int64_t w = int64_t(cus) * pa::kDecodeWavesPerCU;
+  // one workgroup per CU
+  const int64_t w = int64_t(cus) * pa::decode_group_waves(group);
   return std::max<int64_t>(1, std::min(w, tiles_upper));
 }
 
@@ -223,7 +224,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     int cus = 0;
     r = current_cus(&cus);
     if (r != PA_OK) return r;
-    const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len);
+    const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len, group);
     const size_t need = decode_ws_bytes(batch, num_kv_heads, group, waves);
     if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
     if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");

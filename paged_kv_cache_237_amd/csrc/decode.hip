@@ -9,11 +9,23 @@
 // Work decomposition.  Every (sequence, kv head) pair is a "segment" of
 // ceil(ctx/64) tiles of 64 tokens.  All segments are laid end to end and the
 // resulting list of tiles is cut into n_waves equal runs, one per wave, so
-// every wave streams the same number of bytes whatever the length mix.  A run
-// that covers a whole segment writes the bf16 output at once.  A segment cut
-// between runs leaves one partial state (m, l, u) per run in the workspace;
-// each contributing wave then bumps the segment's counter (agent-scope
-// atomic after a release fence) and the last one to arrive merges them:
+// every wave streams the same number of bytes whatever the length mix.  A
+// workgroup holds the waves of one CU; the CU's waves share its bandwidth but
+// are not served evenly, so a wave that gets ahead of its slowest sibling
+// yields issue priority (s_setprio) and the CU's runs end together.
+//
+// A run streams its tiles as one software pipeline: the K loads of the next
+// tile are issued as soon as the current tile's scores are computed and its V
+// loads as soon as the current PV is done, also across segment boundaries
+// (the next segment's q and block-table entry are fetched a tile ahead, the
+// block table and context lengths with scalar loads), so the wave always has
+// a tile's worth of loads in flight.
+//
+// A run that covers a whole segment writes the bf16 output at once.  A
+// segment cut between runs leaves one partial state (m, l, u) per run in the
+// workspace; each contributing wave then bumps the segment's counter
+// (agent-scope atomic once its record stores have completed) and the last one
+// to arrive merges them:
 // M = max m_i,  L = sum 2^(m_i-M) l_i,  o = sum 2^(m_i-M) u_i / L  (the
 // split-context form of the online softmax), and resets the counter to zero,
 // so the workspace counters are zero again after every call.
@@ -31,7 +43,7 @@
 //   * softmax: one wave max per head per tile (DPP rows + 4 lane reads);
 //     scores are kept in the log2 domain (scale * log2 e folded in).
 //   * PV: p goes through LDS to the (row, chunk) layout of V; fp32 FMAs;
-//     the 4 row-partials are folded once per run.
+//     the 4 row-partials are folded once per piece.
 // Memory traffic is the K and V rows of the context read once, plus q and
 // out; the kernel is bound by HBM bandwidth.
 #include <math.h>
@@ -41,7 +53,11 @@
 
 namespace pa {
 
-constexpr int kWavesPerWG = 4;
+template <int G>
+struct GroupShape {
+  static constexpr int kWaves = decode_group_waves(G);  // one workgroup per CU
+  static constexpr int kThreads = kWaves * kWave;
+};
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int n) {
   const int cap = a.mbps * kBlock;
@@ -49,6 +65,15 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int n) {
 }
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
+
+// Load of a value the kernel never writes (block table, context lengths) at a
+// wave-uniform index, through the constant address space: it becomes a
+// scalar load, which is counted apart from the vector loads of K and V, so
+// waiting for it does not wait for the tile loads in flight.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
+  using cint = const __attribute__((address_space(4))) int32_t;
+  return ((cint*)p)[i];
+}
 
 // Number of tiles of all segments (identical in every lane).
 __device__ int total_tiles(const DecodeArgs& a) {
@@ -145,20 +170,84 @@ __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0
   }
 }
 
-template <int G>
-__device__ void decode_run(const DecodeArgs& a, int b, int g, int t_lo, int t_hi, int nt, int wave,
-                           uint4* q_lds, float* p_lds) {
+// Buffer descriptors and offsets of one tile's K and V loads.
+//   K: lane = token; rows past the context get an out-of-range offset and
+//      load zeros (their scores are masked).
+//   V: the buffer ends after the last valid row, so rows past the context
+//      load zeros too (they may hold NaN patterns in memory, which must not
+//      reach p * v).
+struct TileLoads {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t koff, voff;
+  int valid;  // tokens of the tile inside the context (0 for a bad block entry)
+};
+
+__device__ __forceinline__ TileLoads tile_loads(const DecodeArgs& a, int phys, int g, int t, int ctx) {
   const int lane = lane_id();
+  TileLoads tl;
+  const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
+  tl.valid = ok ? min(kTile, ctx - t * kTile) : 0;
+  const int r0 = (t & 3) * kTile;
+  const int64_t bh = (ok ? int64_t(phys) : 0) * a.hkv + g;  // block-head tile index
+  tl.rk = make_rsrc(a.k_cache + bh * (kChunks * kBlock), 65536u);
+  tl.rv = make_rsrc(a.v_cache + bh * (kBlock * kChunks), uint32_t(r0 + tl.valid) * 256u);
+  tl.koff = lane < tl.valid ? uint32_t(r0 + lane) * 16u : kOutOfRange;
+  tl.voff = uint32_t((r0 + (lane >> 4)) * kChunks + (lane & 15)) * 16u;
+  return tl;
+}
+
+__device__ __forceinline__ void issue_k(const TileLoads& tl, uint4 (&kr)[kChunks]) {
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) kr[c] = buf_load16(tl.rk, tl.koff, uint32_t(c) * 4096u);
+}
+
+__device__ __forceinline__ void issue_v(const TileLoads& tl, uint4 (&vr)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) vr[k] = buf_load16(tl.rv, tl.voff + uint32_t(k) * 1024u, 0u);
+}
+
+// Streams tiles [pos, end) of the flattened list (this wave's run) as one
+// software pipeline: the K loads of the next tile are issued as soon as the
+// current tile's scores are computed and its V loads as soon as the current
+// PV is done, also across segment boundaries (the next segment's q and
+// block-table entry are fetched a tile ahead), so the wave always has a
+// tile's worth of loads in flight.  Each piece (run ∩ segment) ends with a
+// fold of the row partials and either the bf16 output (whole segment) or a
+// partial record at seg + wave.  Returns the number of cut segments, whose
+// (b, g, first run, last run) are stored in pend_*.
+template <int G>
+__device__ int stream_run(const DecodeArgs& a, int pos, int end, int per, int wave, uint4* q_lds,
+                          float* p_lds, int* prog, int wv, int (&pend_b)[2], int (&pend_g)[2],
+                          int (&pend_w0)[2], int (&pend_w1)[2]) {
+  constexpr int NW = GroupShape<G>::kWaves;
+  int done = 0;  // tiles streamed by this wave
+  const int lane = lane_id();
+  const int hq = a.hkv * G;
+  constexpr int kQPerLane = (G * kChunks + kWave - 1) / kWave;
+
+  int b, before;
+  locate(a, pos, b, before);
+  if (b >= a.batch) return 0;
+  int nt = tiles_of(clamp_ctx(a, a.ctx_lens[b]));
+  const int off = pos - before * a.hkv;
+  int g = off / nt;
+  int t = off - g * nt;
+  int ctx = clamp_ctx(a, a.ctx_lens[b]);
   b = __builtin_amdgcn_readfirstlane(b);
   g = __builtin_amdgcn_readfirstlane(g);
-  t_lo = __builtin_amdgcn_readfirstlane(t_lo);
-  t_hi = __builtin_amdgcn_readfirstlane(t_hi);
-  const int hq = a.hkv * G;
-  const int ctx = __builtin_amdgcn_readfirstlane(clamp_ctx(a, a.ctx_lens[b]));
+  t = __builtin_amdgcn_readfirstlane(t);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  ctx = __builtin_amdgcn_readfirstlane(ctx);
 
-  // q of the G heads of this kv head: G*256 bytes, staged once per run.
-  const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * hq + g * G) * kDim);
-  for (int i = lane; i < G * kChunks; i += kWave) q_lds[i] = qsrc[i];
+  // prologue: q of the first segment, loads of the first tile
+  {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * hq + g * G) * kDim);
+    for (int i = lane; i < G * kChunks; i += kWave) q_lds[i] = qsrc[i];
+  }
+  TileLoads cur = tile_loads(a, ld_uniform(a.block_table, int64_t(b) * a.mbps + (t >> 2)), g, t, ctx);
+  uint4 kr[kChunks], vr[16];
+  issue_k(cur, kr);
+  issue_v(cur, vr);
   __builtin_amdgcn_wave_barrier();
 
   float m[G], l[G], acc[G][8];
@@ -169,35 +258,60 @@ __device__ void decode_run(const DecodeArgs& a, int b, int g, int t_lo, int t_hi
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
+  const int vrow = lane >> 4;  // row within a 4-row V load
+  int piece_t0 = t;            // first tile of the current piece
+  int npend = 0;
 
-  const int vrow = lane >> 4;   // row within a 4-row V load
-  const int vchunk = lane & 15; // 16-byte chunk within a V row
+  for (; pos < end; ++pos) {
+    // --- where the next tile is (same segment, or the next non-empty one)
+    const bool has_next = pos + 1 < end;
+    int nb = b, ng = g, ntt = t + 1, nnt = nt, nctx = ctx;
+    const bool seg_end = t + 1 == nt;
+    if (seg_end && has_next) {
+      ntt = 0;
+      if (++ng == a.hkv) {
+        ng = 0;
+        nctx = 0;
+        do {
+          nb = __builtin_amdgcn_readfirstlane(nb + 1);
+          nctx = nb < a.batch ? clamp_ctx(a, ld_uniform(a.ctx_lens, nb)) : 0;
+          nnt = nb < a.batch ? tiles_of(nctx) : 1;
+        } while (nnt == 0);
+      }
+    }
+    const bool next_ok = has_next && nb < a.batch;
+    uint4 qn[kQPerLane];
+    if (seg_end && next_ok) {
+      const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(nb) * hq + ng * G) * kDim);
+#pragma unroll
+      for (int j = 0; j < kQPerLane; ++j) {
+        const int i = lane + j * kWave;
+        qn[j] = i < G * kChunks ? qsrc[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    // past the end of the run the "next tile" has no block: its loads are
+    // all out of range and return zeros without touching memory (issuing
+    // them unconditionally lets the registers be reused in place)
+    const int nphys = next_ok ? ld_uniform(a.block_table, int64_t(nb) * a.mbps + (ntt >> 2)) : -1;
 
-  for (int t = t_lo; t < t_hi; ++t) {
-    // q stays in LDS: re-read it every tile (broadcast reads) instead of
-    // letting the compiler hoist G*64 registers of it out of the loop.
+    // The waves of a CU share its bandwidth but are not served evenly; a
+    // wave ahead of its slowest sibling yields issue priority, so that they
+    // progress together and the CU finishes its runs at once.
+    {
+      ++done;
+      if (lane == 0) prog[wv] = done;
+      int slowest = done;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) slowest = min(slowest, prog[w]);
+      if (__builtin_amdgcn_readfirstlane(slowest) + 1 < done)
+        __builtin_amdgcn_s_setprio(0);
+      else
+        __builtin_amdgcn_s_setprio(2);
+    }
+
+    // --- scores of the current tile (q from LDS, broadcast reads)
     asm volatile("" ::: "memory");
-    const int phys = a.block_table[int64_t(b) * a.mbps + (t >> 2)];
-    const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
-    const int valid = ok ? min(kTile, ctx - t * kTile) : 0;
-    const int r0 = (t & 3) * kTile;
-    const int64_t bh = (ok ? int64_t(phys) : 0) * a.hkv + g;  // block-head tile index
-    // K: lane = token; rows past the context get an out-of-range offset and
-    // load zeros (their scores are masked below).  V: the buffer ends after
-    // the last valid row, so rows past the context load zeros too (they may
-    // hold NaN patterns in memory, which must not reach p * v).
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + bh * (kChunks * kBlock), 65536u);
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(a.v_cache + bh * (kBlock * kChunks), uint32_t(r0 + valid) * 256u);
-    const bool kval = lane < valid;
-    const uint32_t koff = kval ? uint32_t(r0 + lane) * 16u : kOutOfRange;
-    const uint32_t voff = uint32_t((r0 + vrow) * kChunks + vchunk) * 16u;
-    uint4 kr[kChunks], vr[16];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) kr[c] = buf_load16(rk, koff, uint32_t(c) * 4096u);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) vr[k] = buf_load16(rv, voff + uint32_t(k) * 1024u, 0u);
-
+    const bool kval = lane < cur.valid;
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.f;
@@ -215,7 +329,12 @@ __device__ void decode_run(const DecodeArgs& a, int b, int g, int t_lo, int t_hi
       for (int h = 0; h < G; ++h) s[h] = dot8_bf16(qb[h], kr[c + 1], dot8_bf16(qa[h], kr[c], s[h]));
       __builtin_amdgcn_sched_barrier(0);
     }
+    // K of the next tile into the registers just freed
+    const TileLoads nxt = tile_loads(a, nphys, ng, ntt, nctx);
+    issue_k(nxt, kr);
+    __builtin_amdgcn_sched_barrier(0);
 
+    // --- online softmax (log2 domain)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       // additive mask: keeps the dot products unconditional (a select on
@@ -233,6 +352,7 @@ __device__ void decode_run(const DecodeArgs& a, int b, int g, int t_lo, int t_hi
     }
     __builtin_amdgcn_wave_barrier();
 
+    // --- PV of the current tile
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float* pp = p_lds + (4 * k + vrow) * G;
@@ -248,60 +368,101 @@ __device__ void decode_run(const DecodeArgs& a, int b, int g, int t_lo, int t_hi
       }
       if (k & 1) __builtin_amdgcn_sched_barrier(0);
     }
+    // V of the next tile into the registers just freed
+    issue_v(nxt, vr);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_wave_barrier();
-  }
 
-  // Fold the 4 row-partials (lanes l, l^16, l^32, l^48 hold the same dims).
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = acc[h][e];
-      x += __shfl_xor(x, 16, kWave);
-      x += __shfl_xor(x, 32, kWave);
-      acc[h][e] = x;
-    }
-    l[h] = wave_sum(l[h]);
-  }
-
-  if (t_lo == 0 && t_hi == nt) {
-    if (lane < 16) {
+    // --- end of a piece: fold, then the output row or a partial record
+    if (seg_end || !has_next) {
+      float lsum[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
-        float o[8];
+        // the 4 row-partials (lanes l, l^16, l^32, l^48 hold the same dims)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = acc[h][e] * inv;
-        uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t(b) * hq + g * G + h) * kDim);
-        dst[lane] = pack8(o);
+        for (int e = 0; e < 8; ++e) {
+          float x = acc[h][e];
+          x += __shfl_xor(x, 16, kWave);
+          x += __shfl_xor(x, 32, kWave);
+          acc[h][e] = x;
+        }
+        lsum[h] = wave_sum(l[h]);
       }
-    }
-  } else {
-    const int seg = b * a.hkv + g;
-    float* rec = a.ws + int64_t(seg + wave) * partial_floats(G);
-    if (lane < 16) {
+      if (piece_t0 == 0 && seg_end) {
+        if (lane < 16) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+          for (int h = 0; h < G; ++h) {
+            const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
+            float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st_coherent(rec + h * kDim + lane * 8 + e, acc[h][e]);
-    }
-    if (lane < G) {
-      float mv = m[0], lv = l[0];
+            for (int e = 0; e < 8; ++e) o[e] = acc[h][e] * inv;
+            uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t(b) * hq + g * G + h) * kDim);
+            dst[lane] = pack8(o);
+          }
+        }
+      } else {
+        const int seg = b * a.hkv + g;
+        float* rec = a.ws + int64_t(seg + wave) * partial_floats(G);
+        if (lane < 16) {
 #pragma unroll
-      for (int h = 1; h < G; ++h)
-        if (lane == h) { mv = m[h]; lv = l[h]; }
-      st_coherent(rec + G * kDim + lane, mv);
-      st_coherent(rec + G * kDim + G + lane, lv);
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st_coherent(rec + h * kDim + lane * 8 + e, acc[h][e]);
+        }
+        if (lane < G) {
+          float mv = m[0], lv = lsum[0];
+#pragma unroll
+          for (int h = 1; h < G; ++h)
+            if (lane == h) { mv = m[h]; lv = lsum[h]; }
+          st_coherent(rec + G * kDim + lane, mv);
+          st_coherent(rec + G * kDim + G + lane, lv);
+        }
+        const int start = pos - t;  // first tile of the segment in the flattened list
+        pend_b[npend] = b;
+        pend_g[npend] = g;
+        pend_w0[npend] = start / per;
+        pend_w1[npend] = (start + nt - 1) / per;
+        ++npend;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+      }
+      piece_t0 = ntt;
+      if (next_ok) {
+        // q of the next segment (loaded a tile ago)
+#pragma unroll
+        for (int j = 0; j < kQPerLane; ++j) {
+          const int i = lane + j * kWave;
+          if (i < G * kChunks) q_lds[i] = qn[j];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
+    if (!next_ok) break;
+    b = nb;
+    g = ng;
+    t = ntt;
+    nt = nnt;
+    ctx = nctx;
+    cur = nxt;
   }
+  return npend;
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  __shared__ uint4 q_lds[kWavesPerWG][G * kChunks];
-  __shared__ float p_lds[kWavesPerWG][kTile * G];
+__global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(DecodeArgs a) {
+  constexpr int NW = GroupShape<G>::kWaves;
+  __shared__ uint4 q_lds[NW][G * kChunks];
+  __shared__ float p_lds[NW][kTile * G];
+  __shared__ int prog[NW];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave = blockIdx.x * kWavesPerWG + wv;
+  const int wave = blockIdx.x * NW + wv;
+  if (lane_id() == 0) prog[wv] = 0;
+  __syncthreads();
 
   // Empty contexts have no tiles: their output rows are zero.
   if (wave < a.n_waves) {
@@ -315,45 +476,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   const int total = total_tiles(a);
   const int per = (total + a.n_waves - 1) / a.n_waves;
-  int pos = wave * per;
+  const int pos = wave * per;
   const int end = min(pos + per, total);
-  if (pos >= end) return;
+  if (pos >= end) {
+    if (lane_id() == 0) prog[wv] = 1 << 30;
+    return;
+  }
 
-  int b, before;
-  locate(a, pos, b, before);
-  if (b >= a.batch) return;
-  int nt = tiles_of(clamp_ctx(a, a.ctx_lens[b]));
-  int off = pos - before * a.hkv;
-  int g = off / nt;
-  int t = off - g * nt;
   // A run cuts at most two segments (its first and its last); their arrivals
   // are counted once the whole run has been streamed, so the record stores
   // never stall the loads.
   int pend_b[2], pend_g[2], pend_w0[2], pend_w1[2];
-  int npend = 0;
-  while (true) {
-    const int take = min(nt - t, end - pos);
-    decode_run<G>(a, b, g, t, t + take, nt, wave, q_lds[wv], p_lds[wv]);
-    if (!(t == 0 && take == nt)) {
-      const int start = pos - t;  // first tile of the segment in the flattened list
-      pend_b[npend] = b;
-      pend_g[npend] = g;
-      pend_w0[npend] = start / per;
-      pend_w1[npend] = (start + nt - 1) / per;
-      ++npend;
-    }
-    pos += take;
-    if (pos >= end) break;
-    t = 0;
-    if (++g == a.hkv) {
-      g = 0;
-      do {
-        ++b;
-        nt = b < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[b])) : 1;
-      } while (nt == 0);
-      if (b >= a.batch) break;
-    }
-  }
+  const int npend = stream_run<G>(a, pos, end, per, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
+                                  pend_g, pend_w0, pend_w1);
+  // a finished wave no longer holds its siblings back
+  if (lane_id() == 0) prog[wv] = 1 << 30;
+  __builtin_amdgcn_s_setprio(0);
 
   if (npend > 0) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -376,8 +514,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
-  const unsigned split_blocks = unsigned((a.n_waves + kWavesPerWG - 1) / kWavesPerWG);
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(split_blocks), dim3(256), 0, s, a);
+  constexpr int NW = GroupShape<G>::kWaves;
+  const unsigned split_blocks = unsigned((a.n_waves + NW - 1) / NW);
+  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -108,6 +108,15 @@ __device__ __forceinline__ int wave_sum_i(int x) {
          (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
 }
 
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_i<kDppXor1>(x));
+  x = max(x, dpp_i<kDppXor2>(x));
+  x = max(x, dpp_i<kDppHalfMirror>(x));
+  x = max(x, dpp_i<kDppMirror>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
 // Inclusive prefix sum across the 64 lanes (lane i gets x_0 + ... + x_i).
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = threadIdx.x & (kWave - 1);

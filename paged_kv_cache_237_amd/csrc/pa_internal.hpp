@@ -63,8 +63,10 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// Waves per CU the decode grid is sized for.
+// Waves per CU the decode grid is sized for.  A workgroup holds the waves of
+// one CU: 8, or 4 for G = 8 (whose waves need twice the registers).
 constexpr int kDecodeWavesPerCU = 8;
+__host__ __device__ constexpr int decode_group_waves(int g) { return g == 8 ? 4 : 8; }
 
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
