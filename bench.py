@@ -103,6 +103,20 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True)
     torch.cuda.synchronize()
     dec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     sto = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    # The same with the caches (4 MB L2 per XCD, 256 MB MALL) flushed between
+    # calls by reading 1 GiB of other data, outside the events: what one layer
+    # of a deep model sees, since its cache is read again only after every
+    # other layer's.  A read leaves clean lines; a write-based flush would
+    # also charge the decode with writing back 256 MB of dirty lines.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        torch.amax(flush, dim=0, out=sink)
+        step(evf[i])
+    torch.cuda.synchronize()
+    dec_flushed = [e[1].elapsed_time(e[2]) for e in evf]
+    del flush, sink
 
     # whole steps
     if graph:
@@ -128,7 +142,7 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True)
     wall = time.perf_counter() - t0
     del dev
     torch.cuda.empty_cache()
-    return wall * 1e3 / steps, dec, sto
+    return wall * 1e3 / steps, dec, sto, dec_flushed
 
 
 def prefill_flops(case: wl.PagedCase) -> int:
@@ -384,7 +398,8 @@ def main(argv=None):
         return 2
     print(f"[bench] {case.name}: B={case.batch} sum_ctx={int(case.context_lens.sum())}",
           file=sys.stderr, flush=True)
-    ms_step, dec_ms, sto_ms = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
+    ms_step, dec_ms, sto_ms, dec_flushed = time_decode(case, args.steps, args.warmup,
+                                                       graph=not args.no_graph)
     copy_probe(args.copy_probe_mib)
     dbytes = decode_bytes(case)
     sbytes = store_bytes(case.batch, case.num_kv_heads)
@@ -413,6 +428,9 @@ def main(argv=None):
         "attended_tokens_per_s": round(sum_ctx / (ms_step * 1e-3), 1),
         "step_launch": "hip graph replay" if not args.no_graph else "eager",
         "decode_ms": round(dec_ms, 4),
+        "decode_ms_caches_flushed": {"median": round(float(np.median(dec_flushed)), 4),
+                                     "min": round(float(np.min(dec_flushed)), 4),
+                                     "max": round(float(np.max(dec_flushed)), 4)},
         "store_ms": round(sto_ms, 4),
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (pa_decode: split-context streaming with fused merge)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -424,9 +442,10 @@ def main(argv=None):
         for name in ("qwen3_4b_decode", "long_context_decode"):
             c = wl.CONFIGS[name]()
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
-            m, d, s = time_decode(c, max(10, args.steps // 5), 3)
+            m, d, s, dfl = time_decode(c, max(10, args.steps // 5), 3)
             b = decode_bytes(c)
             extra[name] = {"decode_ms": round(d, 4), "decode_GBps": round(b / (d * 1e-3) / 1e9, 1),
+                           "decode_ms_caches_flushed_median": round(float(np.median(dfl)), 4),
                            "frac_of_hbm_peak": round(b / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "attended_tokens_per_s": round(int(c.context_lens.sum()) / (d * 1e-3), 1),
                            "sum_context_len": int(c.context_lens.sum())}
