@@ -201,6 +201,24 @@ def prefill_report(steps: int, warmup: int) -> dict:
             "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def varlen_report(name: str, steps: int, warmup: int) -> dict:
+    """pa_prefill on a varlen batch whose rows see long cached contexts
+    (chunked prefill mixed with decode rows; multi-query decode): reported
+    against both rooflines -- causal FLOPs over the bf16 MFMA peak, and the
+    K/V bytes of every context read once over the HBM peak."""
+    c = wl.CONFIGS[name]()
+    sto, pre = time_prefill(c, steps, warmup)
+    fl = prefill_flops(c)
+    kvb = int(c.context_lens.sum()) * c.num_kv_heads * c.head_dim * 2 * 2
+    tf = fl / (pre * 1e-3) / 1e12
+    gbs = kvb / (pre * 1e-3) / 1e9
+    return {"workload": c.name, "prefill_ms": round(pre, 4), "query_rows": c.total_q_rows,
+            "sum_context_len": int(c.context_lens.sum()), "causal_gflop": round(fl / 1e9, 3),
+            "TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "store_ms": round(sto, 4)}
+
+
 # ---------------------------------------------------------------------------
 # Profile summaries (rocprofv3 CSV -> short text/JSON under profiles/)
 
@@ -451,6 +469,9 @@ def main(argv=None):
                            "sum_context_len": int(c.context_lens.sum())}
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(10, args.steps // 5), 3)
+        for name in ("chunked_prefill_mixed", "multi_query_decode"):
+            print(f"[bench] extra {name}", file=sys.stderr, flush=True)
+            extra[name] = varlen_report(name, max(10, args.steps // 5), 3)
         line["extra"] = extra
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -67,6 +67,20 @@ def test_prefill_with_cached_prefix():
     check(wl.make_case("prefix", "prefill", 41, ctx, 16, 8, q_lens=qlens))
 
 
+def test_chunked_prefill_mixed_with_decode_rows():
+    """A chunked-prefill step: 512-token chunks on long cached prefixes mixed
+    with one-token decode rows in one call (every decode row and two chunk
+    sequences checked in full, the other chunks on sampled heads)."""
+    case = wl.chunked_prefill_mixed()
+    check(case, seqs_full=set(range(64)) | {64, 71}, heads_sampled=[0, 7, 12])
+
+
+def test_multi_query_decode():
+    """Speculative verification: 4 new tokens per sequence, causal among
+    themselves, over U{512..4096} cached tokens."""
+    check(wl.multi_query_decode())
+
+
 def test_prefill_stress_peaked_softmax():
     """q scaled by 32: a sharply peaked softmax with |o| up to |v|.  The MFMA
     takes the softmax weights in bf16, so the bar is the error bound derived

@@ -96,6 +96,16 @@ def test_configs_shapes_and_rules():
     assert c5.max_blocks_per_seq == 512
     _check_tables(c5)
 
+    c6 = wl.chunked_prefill_mixed()
+    assert c6.batch == 72 and c6.total_q_rows == 64 + 8 * 512
+    assert np.all(c6.q_lens[:64] == 1) and np.all(c6.q_lens[64:] == 512)
+    assert np.all(c6.context_lens[64:] >= 512 + 512) and np.all(c6.context_lens[64:] <= 8192 + 512)
+    _check_tables(c6)
+
+    c7 = wl.multi_query_decode()
+    assert c7.batch == 64 and np.all(c7.q_lens == 4) and c7.total_q_rows == 256
+    _check_tables(c7)
+
 
 def test_step_and_history_rows_partition_the_cache():
     c = wl.make_case("x", "decode", 5, [1, 4, 300], 4, 2)

@@ -324,12 +324,38 @@ def long_context_decode() -> PagedCase:
     return make_case("long_context_decode", "decode", 5, [131072] * 8, 32, 8)
 
 
+def chunked_prefill_mixed() -> PagedCase:
+    """One step of chunked prefill mixed with decoding: 64 sequences decode one
+    token over U{512..4096} cached tokens, and 8 sequences continue their prompt
+    with a 512-token chunk on top of a cached prefix of U{512..8192} tokens
+    (4,160 query rows); 16 q / 8 kv heads.  Decode rows come first in the
+    batch."""
+    rng = np.random.default_rng(6)
+    dctx = rng.integers(512, 4096, size=64, endpoint=True)
+    prefix = rng.integers(512, 8192, size=8, endpoint=True)
+    ctx = np.concatenate([dctx, prefix + 512])
+    ql = np.concatenate([np.ones(64, dtype=np.int64), np.full(8, 512, dtype=np.int64)])
+    return make_case("chunked_prefill_mixed", "prefill", 6, ctx, 16, 8, q_lens=ql, rng=rng)
+
+
+def multi_query_decode() -> PagedCase:
+    """Speculative verification: 64 sequences each score 4 new tokens (3
+    drafted + 1) over U{512..4096} cached tokens, causally among themselves;
+    16 q / 8 kv heads."""
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(512, 4096, size=64, endpoint=True)
+    return make_case("multi_query_decode", "prefill", 7, ctx, 16, 8,
+                     q_lens=np.full(64, 4, dtype=np.int64), rng=rng)
+
+
 CONFIGS = {
     "tiny_decode": tiny_decode,
     "qwen3_0.6b_decode": qwen3_0_6b_decode,
     "qwen3_4b_decode": qwen3_4b_decode,
     "prefill_8x2048": prefill_8x2048,
     "long_context_decode": long_context_decode,
+    "chunked_prefill_mixed": chunked_prefill_mixed,
+    "multi_query_decode": multi_query_decode,
 }
 
 
