@@ -219,6 +219,57 @@ def varlen_report(name: str, steps: int, warmup: int) -> dict:
             "store_ms": round(sto, 4)}
 
 
+def blocks_report(steps: int, warmup: int) -> dict:
+    """pa_copy_blocks over 512 block pairs of a 2,048-block pool (8 kv heads:
+    1 MiB of K+V per block, so 512 MiB read + 512 MiB written per call), and
+    pa_swap_blocks of 256 blocks to a pinned host pool and back."""
+    nb, hkv, n = 2048, 8, 512
+    k, v = pa.alloc_cache(nb, hkv, "cuda", fill_bits=0x3F80)
+    rng = np.random.default_rng(8)
+    perm = rng.permutation(nb).astype(np.int32)
+    pairs = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], axis=1).copy()).cuda()
+    block_bytes = 2 * hkv * 256 * 128 * 2  # K and V of one block
+    for _ in range(warmup):
+        pa.copy_blocks(k, v, pairs)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        pa.copy_blocks(k, v, pairs)
+        e1.record()
+    torch.cuda.synchronize()
+    cms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    cbytes = 2 * n * block_bytes
+    m = 256
+    hk = torch.empty((m,) + tuple(k.shape[1:]), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty((m,) + tuple(v.shape[1:]), dtype=torch.bfloat16, pin_memory=True)
+    out_pairs = np.stack([perm[:m], np.arange(m, dtype=np.int32)], axis=1)
+    in_pairs = out_pairs[:, ::-1].copy()
+    times = {"out": [], "in": []}
+    for i in range(warmup + steps):
+        for kind, (sk, sv, dk, dv, pp) in (("out", (k, v, hk, hv, out_pairs)),
+                                            ("in", (hk, hv, k, v, in_pairs))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pa.swap_blocks(sk, sv, dk, dv, pp)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times[kind].append(e0.elapsed_time(e1))
+    sbytes = m * block_bytes
+    res = {"copy_blocks_pairs": n, "copy_blocks_ms": round(cms, 4),
+           "copy_blocks_GBps": round(cbytes / (cms * 1e-3) / 1e9, 1),
+           "copy_blocks_frac_of_hbm_peak": round(cbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    for kind in ("out", "in"):
+        t = float(np.median(times[kind]))
+        res[f"swap_{kind}_blocks"] = m
+        res[f"swap_{kind}_ms"] = round(t, 4)
+        res[f"swap_{kind}_GBps"] = round(sbytes / (t * 1e-3) / 1e9, 1)
+    del k, v, hk, hv
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # Profile summaries (rocprofv3 CSV -> short text/JSON under profiles/)
 
@@ -472,6 +523,8 @@ def main(argv=None):
         for name in ("chunked_prefill_mixed", "multi_query_decode"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(10, args.steps // 5), 3)
+        print("[bench] extra block copy / swap", file=sys.stderr, flush=True)
+        extra["blocks"] = blocks_report(max(10, args.steps // 5), 3)
         line["extra"] = extra
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

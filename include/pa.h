@@ -3,7 +3,8 @@
  *
  * C ABI of libpa.so: a slot-mapped store of new keys/values into a cache made
  * of fixed-size blocks, paged decode attention (one query token per sequence)
- * and causal varlen prefill attention over the same paged cache.
+ * and causal varlen prefill attention over the same paged cache, plus whole-
+ * block copies (copy-on-write inside a pool, swap between pools).
  *
  * What the operations compute (no code is taken from these sources):
  *   - nano-vllm hub page (pomoai.com), section "Attention + Triton Kernel":
@@ -89,7 +90,8 @@ enum pa_status {
   PA_ERR_WORKSPACE = -5,     /* workspace missing or too small */
   PA_ERR_HIP = -6,           /* the HIP runtime reported an error */
   PA_ERR_SLOT_RANGE = -7,    /* pa_validate_slots: a slot >= num_slots */
-  PA_ERR_DUPLICATE_SLOT = -8 /* pa_validate_slots: two tokens share a slot */
+  PA_ERR_DUPLICATE_SLOT = -8, /* pa_validate_slots: two tokens share a slot */
+  PA_ERR_BLOCK_CONFLICT = -9  /* pa_validate_block_pairs: a block written twice, or read and written */
 };
 
 /*
@@ -180,6 +182,65 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
                int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole cache blocks inside one pool (copy-on-write of
+ * a block shared by several sequences before one of them extends it).
+ *
+ * For every pair i < n_pairs with (src, dst) = (pairs[2i], pairs[2i+1]), both
+ * indexes in [0, num_blocks) and src != dst: block dst of the K cache and of
+ * the V cache (all kv heads) receives a bit copy of block src.  Pairs with an
+ * index outside the pool (e.g. -1 padding) or src == dst are skipped.
+ *
+ *   k_cache, v_cache : the pools, layouts above, num_blocks blocks each.
+ *   pairs         : DEVICE int32 [n_pairs][2], 4-B aligned.
+ *   Precondition (not checked on the device; pa_validate_block_pairs checks
+ *   it on the host): no block is the destination of two pairs or both a
+ *   source and a destination in one call -- otherwise the result depends on
+ *   the order of the copies.
+ *   Source: CSDN essay comparing nanoVLLM and vLLM, first section (blocks
+ *   are allocated per sequence through the block table; vLLM's block
+ *   management).
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t n_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, void* stream);
+
+/*
+ * pa_swap_blocks -- copy whole blocks between two pools of the same layout,
+ * typically the device cache and a pinned host cache (swap-out for
+ * preemption and swap-in when the sequence resumes).
+ *
+ * For every pair i, block host_pairs[2i+1] of (dst_k, dst_v) receives a bit
+ * copy of block host_pairs[2i] of (src_k, src_v).  Runs of pairs whose source
+ * and destination both advance by one block become one transfer.  The copies
+ * are asynchronous DMA transfers on `stream` (no kernel); host pools should be
+ * pinned (hipHostMalloc) for them to overlap with other work.
+ *
+ *   src_k, src_v, dst_k, dst_v : pools with src_num_blocks / dst_num_blocks
+ *                   blocks, each a device pointer or a host pointer known to
+ *                   the HIP runtime; source and destination pools are
+ *                   different allocations.
+ *   host_pairs    : HOST int32 [n_pairs][2] (src block, dst block); every
+ *                   index must lie in its pool (else PA_ERR_SLOT_RANGE and
+ *                   nothing is copied).  Destinations should be distinct.
+ *   Source: CSDN essay comparing nanoVLLM and vLLM, first and closing
+ *   sections (vLLM swaps KV cache out to CPU memory under memory pressure
+ *   and back in later; nano-vllm has no swap).
+ */
+int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int32_t* host_pairs, int64_t n_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, void* stream);
+
+/*
+ * pa_validate_block_pairs -- host-side check of a pa_copy_blocks pair list
+ * (HOST int32 [n_pairs][2]).  Pairs that pa_copy_blocks skips (a negative
+ * index or src == dst) are ignored.  Returns PA_ERR_SLOT_RANGE if an index is
+ * >= num_blocks, PA_ERR_BLOCK_CONFLICT if a block is the destination of two
+ * pairs or both a source and a destination, PA_OK otherwise.
+ */
+int pa_validate_block_pairs(const int32_t* host_pairs, int64_t n_pairs, int64_t num_blocks);
 
 /* Name of a status code ("PA_OK", "PA_ERR_NULL_PTR", ...); never NULL. */
 const char* pa_status_string(int status);

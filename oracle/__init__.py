@@ -9,6 +9,7 @@ from .paged_attention import (  # noqa: F401
     CHUNK,
     attend,
     bf16_to_f64,
+    copy_blocks,
     decode,
     decode_seq,
     gather_seq,

@@ -36,6 +36,9 @@ Readings where the pages are silent (each is a test-pinned choice):
     ctx_b - q_len_b + i and sees keys 0..that position (bottom-right causal);
   * an empty context (ctx = 0) gives a zero output row.
 
+Block copies (copy_blocks) follow the same bit-copy rule for whole blocks;
+vLLM's swap between GPU and CPU memory moves whole blocks the same way.
+
 Pins (tests/test_oracle.py): layout offsets written out by hand; store round
 trip and untouched bytes; equality with torch's float64 scaled-dot-product
 attention on contiguous caches; bit-identical results under any permutation
@@ -91,6 +94,22 @@ def store_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: n
         blk, row = divmod(s, bs)
         k_pool[blk, :, :, row, :] = k_new[i].reshape(hkv, nchunk, CHUNK)
         v_pool[blk, :, row, :] = v_new[i]
+
+
+def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs) -> None:
+    """Copy whole blocks inside the pools: for each (src, dst) with both in
+    range and src != dst, block dst (all kv heads, K and V) becomes a bit copy
+    of block src.  Other pairs are skipped.  In place; the pairs are read in
+    order, and a valid list writes no block twice and never reads a block it
+    writes, so the order does not matter for it.  (CSDN essay, first section:
+    blocks belong to sequences through the block table; a block shared by two
+    sequences is copied before one of them writes to it.)"""
+    nb = k_pool.shape[0]
+    for src, dst in np.asarray(pairs, np.int64).reshape(-1, 2):
+        if src < 0 or dst < 0 or src >= nb or dst >= nb or src == dst:
+            continue
+        k_pool[dst] = k_pool[src]
+        v_pool[dst] = v_pool[src]
 
 
 def gather_seq(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray, n: int):

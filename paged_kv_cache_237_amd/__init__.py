@@ -30,10 +30,11 @@ PA_OK = 0
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL_PTR", -2: "PA_ERR_BAD_SHAPE", -3: "PA_ERR_UNSUPPORTED",
     -4: "PA_ERR_ALIGN", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP", -7: "PA_ERR_SLOT_RANGE",
-    -8: "PA_ERR_DUPLICATE_SLOT",
+    -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT",
 }
 
 EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_prefill",
+           "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
            "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
 
 
@@ -78,6 +79,13 @@ def lib() -> ctypes.CDLL:
         l.pa_last_error_detail.restype = ctypes.c_char_p
         l.pa_validate_slots.argtypes = [_vp, _i64, _i64]
         l.pa_validate_slots.restype = ctypes.c_int
+        l.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp]
+        l.pa_copy_blocks.restype = ctypes.c_int
+        l.pa_swap_blocks.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                     _vp]
+        l.pa_swap_blocks.restype = ctypes.c_int
+        l.pa_validate_block_pairs.argtypes = [_vp, _i64, _i64]
+        l.pa_validate_block_pairs.restype = ctypes.c_int
         _lib = l
     return _lib
 
@@ -203,3 +211,48 @@ def validate_slots(slots_host, num_slots: int) -> int:
     import numpy as np
     arr = np.ascontiguousarray(np.asarray(slots_host, dtype=np.int32))
     return int(lib().pa_validate_slots(arr.ctypes.data if arr.size else None, arr.size, num_slots))
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """pa_copy_blocks: pairs int32 [n, 2] (src, dst) on the GPU."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    _check(lib().pa_copy_blocks(
+        _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(pairs, "pairs", _I32), int(pairs.shape[0]), nb, BLOCK_SIZE, hkv, HEAD_DIM,
+        _stream(k_cache, stream)))
+
+
+def _pool_ptr(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _BF16:
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs_host, stream=None) -> None:
+    """pa_swap_blocks: copy whole blocks between two pools of the same layout
+    (device or pinned host tensors); pairs_host is a host int32 [n, 2] array
+    of (src block, dst block).  Asynchronous on the stream of the device
+    pool."""
+    import numpy as np
+    snb, hkv = _cache_geometry(src_k, src_v)
+    dnb, hkv2 = _cache_geometry(dst_k, dst_v)
+    if hkv != hkv2:
+        raise ValueError("pools have different kv head counts")
+    arr = np.ascontiguousarray(np.asarray(pairs_host, dtype=np.int32).reshape(-1, 2))
+    dev_t = src_k if src_k.is_cuda else dst_k
+    _check(lib().pa_swap_blocks(
+        _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"), _pool_ptr(dst_k, "dst_k"),
+        _pool_ptr(dst_v, "dst_v"), arr.ctypes.data if arr.size else None, arr.shape[0], snb, dnb,
+        BLOCK_SIZE, hkv, HEAD_DIM, _stream(dev_t, stream)))
+
+
+def validate_block_pairs(pairs_host, num_blocks: int) -> int:
+    """pa_validate_block_pairs on a host int32 [n, 2] array; returns the status code."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(pairs_host, dtype=np.int32).reshape(-1, 2))
+    return int(lib().pa_validate_block_pairs(arr.ctypes.data if arr.size else None, arr.shape[0],
+                                             num_blocks))

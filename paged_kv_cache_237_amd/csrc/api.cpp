@@ -112,6 +112,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "PA_ERR_HIP";
     case PA_ERR_SLOT_RANGE: return "PA_ERR_SLOT_RANGE";
     case PA_ERR_DUPLICATE_SLOT: return "PA_ERR_DUPLICATE_SLOT";
+    case PA_ERR_BLOCK_CONFLICT: return "PA_ERR_BLOCK_CONFLICT";
     default: return "PA_ERR_UNKNOWN";
   }
 }
@@ -140,6 +141,115 @@ int pa_validate_slots(const int32_t* host_slots, int64_t n, int64_t num_slots) {
     return ok();
   } catch (...) {
     return fail(PA_ERR_BAD_SHAPE, "host allocation failed");
+  }
+}
+
+int pa_validate_block_pairs(const int32_t* host_pairs, int64_t n_pairs, int64_t num_blocks) {
+  try {
+    if (n_pairs < 0 || num_blocks < 0) return fail(PA_ERR_BAD_SHAPE, "negative size");
+    if (n_pairs == 0) return ok();
+    if (host_pairs == nullptr) return fail(PA_ERR_NULL_PTR, "host_pairs is NULL");
+    std::vector<int32_t> srcs, dsts;
+    for (int64_t i = 0; i < n_pairs; ++i) {
+      const int32_t a = host_pairs[2 * i], b = host_pairs[2 * i + 1];
+      if (a < 0 || b < 0 || a == b) continue;  // skipped by the copy
+      if (int64_t(a) >= num_blocks || int64_t(b) >= num_blocks)
+        return fail(PA_ERR_SLOT_RANGE, "pair " + std::to_string(i) + " = (" + std::to_string(a) +
+                                           ", " + std::to_string(b) + ") outside " +
+                                           std::to_string(num_blocks) + " blocks");
+      srcs.push_back(a);
+      dsts.push_back(b);
+    }
+    std::sort(dsts.begin(), dsts.end());
+    for (size_t i = 1; i < dsts.size(); ++i)
+      if (dsts[i] == dsts[i - 1])
+        return fail(PA_ERR_BLOCK_CONFLICT, "block " + std::to_string(dsts[i]) +
+                                               " is the destination of two pairs");
+    std::sort(srcs.begin(), srcs.end());
+    for (int32_t d : dsts)
+      if (std::binary_search(srcs.begin(), srcs.end(), d))
+        return fail(PA_ERR_BLOCK_CONFLICT, "block " + std::to_string(d) +
+                                               " is both a source and a destination");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_BAD_SHAPE, "host allocation failed");
+  }
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int64_t n_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, void* stream) {
+  try {
+    if (n_pairs < 0) return fail(PA_ERR_BAD_SHAPE, "n_pairs < 0");
+    if (num_kv_heads <= 0 || num_kv_heads > 65535)
+      return fail(PA_ERR_BAD_SHAPE, "num_kv_heads must be in 1..65535");
+    if (head_dim != PA_HEAD_DIM) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+    if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_UNSUPPORTED, "block_size must be 256");
+    if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
+    if (n_pairs == 0) return ok();
+    if (n_pairs > INT32_MAX) return fail(PA_ERR_BAD_SHAPE, "n_pairs too large");
+    if (!k_cache || !v_cache || !pairs)
+      return fail(PA_ERR_NULL_PTR, "pa_copy_blocks: a pointer argument is NULL");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pairs, 4))
+      return fail(PA_ERR_ALIGN, "caches must be 16-byte aligned, pairs 4-byte");
+    pa::CopyBlocksArgs a;
+    a.pairs = pairs;
+    a.n_pairs = n_pairs;
+    a.k_cache = static_cast<uint4*>(k_cache);
+    a.v_cache = static_cast<uint4*>(v_cache);
+    a.num_blocks = num_blocks;
+    a.hkv = num_kv_heads;
+    const hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected host exception");
+  }
+}
+
+int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int32_t* host_pairs, int64_t n_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, void* stream) {
+  try {
+    if (n_pairs < 0) return fail(PA_ERR_BAD_SHAPE, "n_pairs < 0");
+    if (num_kv_heads <= 0) return fail(PA_ERR_BAD_SHAPE, "num_kv_heads must be positive");
+    if (head_dim != PA_HEAD_DIM) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128");
+    if (block_size != PA_BLOCK_SIZE) return fail(PA_ERR_UNSUPPORTED, "block_size must be 256");
+    if (src_num_blocks <= 0 || dst_num_blocks <= 0)
+      return fail(PA_ERR_BAD_SHAPE, "pools must have a positive number of blocks");
+    if (n_pairs == 0) return ok();
+    if (!src_k || !src_v || !dst_k || !dst_v || !host_pairs)
+      return fail(PA_ERR_NULL_PTR, "pa_swap_blocks: a pointer argument is NULL");
+    for (int64_t i = 0; i < n_pairs; ++i) {
+      const int32_t a = host_pairs[2 * i], b = host_pairs[2 * i + 1];
+      if (a < 0 || int64_t(a) >= src_num_blocks || b < 0 || int64_t(b) >= dst_num_blocks)
+        return fail(PA_ERR_SLOT_RANGE, "pair " + std::to_string(i) + " = (" + std::to_string(a) +
+                                           ", " + std::to_string(b) + ") outside its pool");
+    }
+    // one block of one cache, all kv heads: contiguous in both layouts
+    const size_t bytes = size_t(num_kv_heads) * PA_BLOCK_SIZE * PA_HEAD_DIM * 2;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // runs of consecutive (src, dst) blocks become one transfer
+    int64_t i = 0;
+    while (i < n_pairs) {
+      int64_t j = i + 1;
+      while (j < n_pairs && host_pairs[2 * j] == host_pairs[2 * i] + (j - i) &&
+             host_pairs[2 * j + 1] == host_pairs[2 * i + 1] + (j - i))
+        ++j;
+      const size_t so = size_t(host_pairs[2 * i]) * bytes, dof = size_t(host_pairs[2 * i + 1]) * bytes;
+      const size_t len = size_t(j - i) * bytes;
+      hipError_t e = hipMemcpyAsync(static_cast<char*>(dst_k) + dof,
+                                    static_cast<const char*>(src_k) + so, len, hipMemcpyDefault, st);
+      if (e != hipSuccess) return hip_fail(e, "swap K copy");
+      e = hipMemcpyAsync(static_cast<char*>(dst_v) + dof, static_cast<const char*>(src_v) + so, len,
+                         hipMemcpyDefault, st);
+      if (e != hipSuccess) return hip_fail(e, "swap V copy");
+      i = j;
+    }
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected host exception");
   }
 }
 

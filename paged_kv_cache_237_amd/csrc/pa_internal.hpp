@@ -63,12 +63,22 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+struct CopyBlocksArgs {
+  const int32_t* pairs;  // [n_pairs][2] (src, dst)
+  int64_t n_pairs;
+  uint4* k_cache;
+  uint4* v_cache;
+  int64_t num_blocks;
+  int hkv;
+};
+
 // Waves per CU the decode grid is sized for.  A workgroup holds the waves of
 // one CU: 8, or 4 for G = 8 (whose waves need twice the registers).
 constexpr int kDecodeWavesPerCU = 8;
 __host__ __device__ constexpr int decode_group_waves(int g) { return g == 8 ? 4 : 8; }
 
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t s);
 

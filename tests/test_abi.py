@@ -131,3 +131,56 @@ def test_validate_slots():
     assert pa.validate_slots([3, 1, 3], 8) == -8
     assert pa.validate_slots([], 8) == 0
     assert pa.validate_slots(np.arange(1000, dtype=np.int32), 1000) == 0
+
+
+@needs_lib
+def test_copy_blocks_rejects_bad_arguments_on_the_host():
+    lib = pa.lib()
+    base = dict(kc=FAKE, vc=FAKE, p=FAKE, n=3, nb=8, bs=256, hkv=8, d=128)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return lib.pa_copy_blocks(a["kc"], a["vc"], a["p"], a["n"], a["nb"], a["bs"], a["hkv"],
+                                  a["d"], None)
+
+    assert call(n=0) == 0
+    assert call(n=-1) == -2
+    assert call(hkv=0) == -2
+    assert call(d=64) == -3
+    assert call(bs=512) == -3
+    assert call(nb=0) == -2
+    assert call(p=None) == -1
+    assert call(kc=FAKE + 8) == -4
+    assert call(p=FAKE + 2) == -4
+
+
+@needs_lib
+def test_swap_blocks_rejects_bad_arguments_on_the_host():
+    lib = pa.lib()
+    pairs = np.array([[0, 1], [1, 2]], dtype=np.int32)
+    bad = np.array([[0, 1], [9, 2]], dtype=np.int32)
+    base = dict(sk=FAKE, sv=FAKE, dk=FAKE, dv=FAKE, p=pairs.ctypes.data, n=2, snb=8, dnb=4,
+                bs=256, hkv=8, d=128)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return lib.pa_swap_blocks(a["sk"], a["sv"], a["dk"], a["dv"], a["p"], a["n"], a["snb"],
+                                  a["dnb"], a["bs"], a["hkv"], a["d"], None)
+
+    assert call(n=0) == 0
+    assert call(n=-1) == -2
+    assert call(snb=0) == -2
+    assert call(d=256) == -3
+    assert call(dk=None) == -1
+    assert call(p=bad.ctypes.data) == -7       # source block 9 outside an 8-block pool
+    assert call(dnb=2) == -7                   # destination block 2 outside a 2-block pool
+    assert b"outside" in lib.pa_last_error_detail()
+
+
+@needs_lib
+def test_validate_block_pairs():
+    assert pa.validate_block_pairs([[0, 3], [1, 4], [-1, 5], [2, 2]], 8) == 0
+    assert pa.validate_block_pairs([[0, 8]], 8) == -7
+    assert pa.validate_block_pairs([[0, 3], [1, 3]], 8) == -9      # block 3 written twice
+    assert pa.validate_block_pairs([[0, 3], [3, 5]], 8) == -9      # block 3 read and written
+    assert pa.validate_block_pairs(np.zeros((0, 2), np.int32), 8) == 0

@@ -102,6 +102,26 @@ def test_store_writes_only_its_slots_and_skips_negative():
                 assert np.all(vp[blk, :, row, :] == POISON)
 
 
+def test_copy_blocks_moves_whole_blocks_and_skips_invalid_pairs():
+    """Tokens stored into the source blocks read back, through a table that
+    points at the destinations, exactly; untouched blocks keep their bytes;
+    pairs with a negative or out-of-pool index or src == dst do nothing."""
+    rng = np.random.default_rng(11)
+    nb, hkv, d, bs = 6, 2, 16, 4
+    kp, vp = oracle.new_pools(nb, hkv, d, bs, POISON)
+    n = 2 * bs  # fill blocks 0 and 2 completely
+    slots = np.concatenate([np.arange(0, bs), np.arange(2 * bs, 3 * bs)]).astype(np.int32)
+    k_new, v_new = rand_bits(rng, (n, hkv, d)), rand_bits(rng, (n, hkv, d))
+    oracle.store_kv(kp, vp, k_new, v_new, slots)
+    k_before, v_before = kp.copy(), vp.copy()
+    oracle.copy_blocks(kp, vp, [[0, 4], [2, 5], [-1, 1], [1, 1], [6, 3], [0, -2]])
+    kg, vg = oracle.gather_seq(kp, vp, np.array([4, 5], np.int32), n)
+    assert np.array_equal(kg, k_new) and np.array_equal(vg, v_new)
+    for blk in (0, 1, 2, 3):
+        assert np.array_equal(kp[blk], k_before[blk]) and np.array_equal(vp[blk], v_before[blk])
+    assert np.all(kp[1] == POISON) and np.all(vp[3] == POISON)
+
+
 def test_store_then_gather_round_trip():
     case = small_case(11, [1, 3, 4, 5, 9], 4, 2)
     q, k, v = case_tensors(case)
