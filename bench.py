@@ -270,6 +270,43 @@ def blocks_report(steps: int, warmup: int) -> dict:
     return res
 
 
+def block_manager_report(steps: int = 512) -> dict:
+    """Host cost of the block manager in a decode loop: the batch of the
+    256-sequence decode workload (its context lengths as prompts, every
+    other sequence forked from its neighbour so that copy-on-write happens),
+    then `steps` decode steps, each one pa_bm_append_batch for the whole
+    batch plus the step's block table (pa_bm_block_table).  Also the same
+    appends made one pa_bm_append call per sequence, for comparison."""
+    case = wl.CONFIGS["qwen3_4b_decode"]()
+    lens = [int(x) for x in case.context_lens]
+    res = {"batch": len(lens), "steps": steps}
+    for mode in ("batched", "per_sequence"):
+        need = sum(-(-(n + steps) // 256) for n in lens) + len(lens)
+        bm = pa.BlockManager(need)
+        for i, n in enumerate(lens):
+            if i % 2 == 1:
+                bm.fork(i - 1, i)
+            else:
+                bm.allocate(i, n)
+        seqs = list(range(len(lens)))
+        width = -(-(max(lens) + steps) // 256)
+        copies = 0
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            if mode == "batched":
+                _, pairs = bm.append_batch(seqs)
+                copies += len(pairs)
+            else:
+                for q in seqs:
+                    copies += bm.append(q)[1] is not None
+            bm.block_table(seqs, width)
+        dt = time.perf_counter() - t0
+        res[f"{mode}_us_per_step"] = round(dt / steps * 1e6, 2)
+        res[f"{mode}_appends_per_s"] = round(steps * len(lens) / dt, 1)
+        res[f"{mode}_copy_pairs"] = copies
+    return res
+
+
 # ---------------------------------------------------------------------------
 # Profile summaries (rocprofv3 CSV -> short text/JSON under profiles/)
 
@@ -525,6 +562,8 @@ def main(argv=None):
             extra[name] = varlen_report(name, max(10, args.steps // 5), 3)
         print("[bench] extra block copy / swap", file=sys.stderr, flush=True)
         extra["blocks"] = blocks_report(max(10, args.steps // 5), 3)
+        print("[bench] extra block manager (host)", file=sys.stderr, flush=True)
+        extra["block_manager"] = block_manager_report()
         line["extra"] = extra
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -91,7 +91,8 @@ enum pa_status {
   PA_ERR_HIP = -6,           /* the HIP runtime reported an error */
   PA_ERR_SLOT_RANGE = -7,    /* pa_validate_slots: a slot >= num_slots */
   PA_ERR_DUPLICATE_SLOT = -8, /* pa_validate_slots: two tokens share a slot */
-  PA_ERR_BLOCK_CONFLICT = -9  /* pa_validate_block_pairs: a block written twice, or read and written */
+  PA_ERR_BLOCK_CONFLICT = -9, /* pa_validate_block_pairs: a block written twice, or read and written */
+  PA_ERR_NO_BLOCKS = -10      /* block manager: not enough free blocks */
 };
 
 /*
@@ -241,6 +242,73 @@ int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_
  * pairs or both a source and a destination, PA_OK otherwise.
  */
 int pa_validate_block_pairs(const int32_t* host_pairs, int64_t n_pairs, int64_t num_blocks);
+
+/*
+ * Host block manager -- the bookkeeping that produces block tables and slot
+ * mappings for the calls above (host memory only; no GPU work).
+ *
+ * Source: nano-vllm hub page, "KV Cache block management" (blocks of a fixed
+ * 256 tokens, allocated and released with reference counts); CSDN essay
+ * comparing nanoVLLM and vLLM, first section (a per-sequence block table of
+ * physical blocks allocated on demand: a sequence takes a new block each time
+ * its length reaches 256k+1).
+ *
+ * Sequences are named by caller-chosen int64 ids.  Free blocks are handed out
+ * first-in first-out, starting from block 0 (released blocks join the end).
+ * Every call is serialised by a mutex inside the manager; all pointers are
+ * HOST pointers.  Errors return a negative PA_ERR_* code (detail in
+ * pa_last_error_detail) and leave the manager unchanged.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens (every slot must fit
+ * an int32); NULL on bad arguments. */
+pa_block_manager* pa_bm_create(int64_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Blocks currently free (-1 for a NULL manager). */
+int64_t pa_bm_num_free(pa_block_manager* bm);
+
+/* New sequence `seq` holding num_tokens tokens (e.g. a prompt):
+ * ceil(num_tokens / block_size) blocks.  PA_ERR_NO_BLOCKS if too few are
+ * free, PA_ERR_BAD_SHAPE if seq exists. */
+int pa_bm_allocate(pa_block_manager* bm, int64_t seq, int64_t num_tokens);
+
+/* One more token for `seq`: *slot_out receives its cache slot.  When the new
+ * length is k*block_size + 1 a new block is taken; otherwise, if the last
+ * block is shared with another sequence, a private copy is taken first and
+ * copy_pair_out[0..1] = (shared block, new block) -- the caller copies it
+ * with pa_copy_blocks before storing; else copy_pair_out = (-1, -1). */
+int pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t* slot_out, int32_t* copy_pair_out);
+
+/* pa_bm_append for every sequence of a decode step, in the order given, as one
+ * all-or-nothing call: slots_out[i] receives the slot of seqs[i]'s new token;
+ * the copy pairs the step produced are packed into pairs_out[0 .. 2*k) (room
+ * for 2*n int32 must be there) and *n_pairs_out = k -- a list ready for
+ * pa_copy_blocks, which must run before the step's tokens are stored.  The
+ * blocks the batch needs are counted first: PA_ERR_NO_BLOCKS if too few are
+ * free, PA_ERR_BAD_SHAPE if a sequence is unknown or listed twice; either way
+ * nothing changes. */
+int pa_bm_append_batch(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
+                       int32_t* pairs_out, int32_t* n_pairs_out);
+
+/* `child` shares every block of `parent` (reference counts + 1). */
+int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+
+/* Release `seq`: reference counts - 1; blocks reaching zero become free. */
+int pa_bm_free(pa_block_manager* bm, int64_t seq);
+
+/* Tokens held by `seq` (-1 if unknown). */
+int64_t pa_bm_seq_len(pa_block_manager* bm, int64_t seq);
+
+/* Rows of an int32 [n][max_blocks_per_seq] block table (-1 padded) for the
+ * n sequences seqs[0..n); PA_ERR_BAD_SHAPE if one needs more columns. */
+int pa_bm_block_table(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t* table_out,
+                      int32_t max_blocks_per_seq);
+
+/* Cache slots of positions first_pos .. first_pos+count-1 of `seq`. */
+int pa_bm_slot_mapping(pa_block_manager* bm, int64_t seq, int64_t first_pos, int64_t count,
+                       int32_t* slots_out);
 
 /* Name of a status code ("PA_OK", "PA_ERR_NULL_PTR", ...); never NULL. */
 const char* pa_status_string(int status);

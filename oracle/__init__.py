@@ -5,6 +5,7 @@ leg may import this package.  The product path (the HIP library and its
 Python binding) never does, and this package never imports them.
 """
 
+from .block_manager import BlockManagerModel  # noqa: F401
 from .paged_attention import (  # noqa: F401
     CHUNK,
     attend,

@@ -30,11 +30,13 @@ PA_OK = 0
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL_PTR", -2: "PA_ERR_BAD_SHAPE", -3: "PA_ERR_UNSUPPORTED",
     -4: "PA_ERR_ALIGN", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP", -7: "PA_ERR_SLOT_RANGE",
-    -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT",
+    -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT", -10: "PA_ERR_NO_BLOCKS",
 }
 
 EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_prefill",
            "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
+           "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append",
+           "pa_bm_append_batch", "pa_bm_fork", "pa_bm_free", "pa_bm_seq_len", "pa_bm_block_table", "pa_bm_slot_mapping",
            "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
 
 
@@ -86,6 +88,28 @@ def lib() -> ctypes.CDLL:
         l.pa_swap_blocks.restype = ctypes.c_int
         l.pa_validate_block_pairs.argtypes = [_vp, _i64, _i64]
         l.pa_validate_block_pairs.restype = ctypes.c_int
+        l.pa_bm_create.argtypes = [_i64, _i32]
+        l.pa_bm_create.restype = _vp
+        l.pa_bm_destroy.argtypes = [_vp]
+        l.pa_bm_destroy.restype = None
+        l.pa_bm_num_free.argtypes = [_vp]
+        l.pa_bm_num_free.restype = _i64
+        l.pa_bm_allocate.argtypes = [_vp, _i64, _i64]
+        l.pa_bm_allocate.restype = ctypes.c_int
+        l.pa_bm_append.argtypes = [_vp, _i64, _vp, _vp]
+        l.pa_bm_append.restype = ctypes.c_int
+        l.pa_bm_append_batch.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
+        l.pa_bm_append_batch.restype = ctypes.c_int
+        l.pa_bm_fork.argtypes = [_vp, _i64, _i64]
+        l.pa_bm_fork.restype = ctypes.c_int
+        l.pa_bm_free.argtypes = [_vp, _i64]
+        l.pa_bm_free.restype = ctypes.c_int
+        l.pa_bm_seq_len.argtypes = [_vp, _i64]
+        l.pa_bm_seq_len.restype = _i64
+        l.pa_bm_block_table.argtypes = [_vp, _vp, _i32, _vp, _i32]
+        l.pa_bm_block_table.restype = ctypes.c_int
+        l.pa_bm_slot_mapping.argtypes = [_vp, _i64, _i64, _i64, _vp]
+        l.pa_bm_slot_mapping.restype = ctypes.c_int
         _lib = l
     return _lib
 
@@ -256,3 +280,74 @@ def validate_block_pairs(pairs_host, num_blocks: int) -> int:
     arr = np.ascontiguousarray(np.asarray(pairs_host, dtype=np.int32).reshape(-1, 2))
     return int(lib().pa_validate_block_pairs(arr.ctypes.data if arr.size else None, arr.shape[0],
                                              num_blocks))
+
+
+class BlockManager:
+    """The library's host block manager (pa_bm_*): fixed-size blocks with
+    reference counts, on-demand growth at 256k+1 tokens, copy-on-write of a
+    shared last block, fork and free; emits block tables and slot mappings."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        self._h = lib().pa_bm_create(num_blocks, block_size)
+        if not self._h:
+            raise PAError(-2, lib().pa_last_error_detail().decode())
+        self._destroy = lib().pa_bm_destroy  # still callable at interpreter exit
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._destroy(h)
+            self._h = None
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_bm_num_free(self._h))
+
+    def allocate(self, seq: int, num_tokens: int) -> None:
+        _check(lib().pa_bm_allocate(self._h, seq, num_tokens))
+
+    def append(self, seq: int):
+        """One more token; returns (slot, copy_pair or None)."""
+        slot = ctypes.c_int32(0)
+        pair = (ctypes.c_int32 * 2)()
+        _check(lib().pa_bm_append(self._h, seq, ctypes.byref(slot), pair))
+        return int(slot.value), (None if pair[0] < 0 else (int(pair[0]), int(pair[1])))
+
+    def append_batch(self, seqs):
+        """One token for each of seqs, all or nothing; returns (slots int32
+        [n], copy pairs int32 [k, 2])."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = len(ids)
+        slots = np.empty(n, dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        k = ctypes.c_int32(0)
+        _check(lib().pa_bm_append_batch(self._h, ids.ctypes.data if n else None, n,
+                                        slots.ctypes.data, pairs.ctypes.data, ctypes.byref(k)))
+        return slots, pairs[:k.value].copy()
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pa_bm_fork(self._h, parent, child))
+
+    def free(self, seq: int) -> None:
+        _check(lib().pa_bm_free(self._h, seq))
+
+    def seq_len(self, seq: int) -> int:
+        return int(lib().pa_bm_seq_len(self._h, seq))
+
+    def block_table(self, seqs, max_blocks_per_seq: int):
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        out = np.empty((len(ids), max_blocks_per_seq), dtype=np.int32)
+        _check(lib().pa_bm_block_table(self._h, ids.ctypes.data if ids.size else None, len(ids),
+                                       out.ctypes.data, max_blocks_per_seq))
+        return out
+
+    def slot_mapping(self, seq: int, first_pos: int, count: int):
+        import numpy as np
+        out = np.empty(count, dtype=np.int32)
+        _check(lib().pa_bm_slot_mapping(self._h, seq, first_pos, count,
+                                        out.ctypes.data if count else None))
+        return out

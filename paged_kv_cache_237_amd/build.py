@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "prefill.hip", "blocks.hip"]
+SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "prefill.hip", "blocks.hip",
+           "block_manager.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5",

@@ -25,6 +25,14 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+}  // namespace
+
+namespace pa {
+int report_error(int code, const std::string& msg) { return fail(code, msg); }
+}  // namespace pa
+
+namespace {
+
 int ok() {
   g_detail.clear();
   return PA_OK;
@@ -113,6 +121,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_SLOT_RANGE: return "PA_ERR_SLOT_RANGE";
     case PA_ERR_DUPLICATE_SLOT: return "PA_ERR_DUPLICATE_SLOT";
     case PA_ERR_BLOCK_CONFLICT: return "PA_ERR_BLOCK_CONFLICT";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS";
     default: return "PA_ERR_UNKNOWN";
   }
 }

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace pa {
 
 constexpr int kBlock = 256;      // tokens per cache block
@@ -76,6 +78,10 @@ struct CopyBlocksArgs {
 // one CU: 8, or 4 for G = 8 (whose waves need twice the registers).
 constexpr int kDecodeWavesPerCU = 8;
 __host__ __device__ constexpr int decode_group_waves(int g) { return g == 8 ? 4 : 8; }
+
+// Records a status and its detail string for pa_last_error_detail (thread
+// local); returns the status.
+int report_error(int code, const std::string& msg);
 
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
