@@ -365,6 +365,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     a.hkv = num_kv_heads;
     a.mbps = max_blocks_per_seq;
     a.n_waves = int(waves);
+    a.run_w_even = pa::kRunWeightEven;
+    a.run_w_odd = pa::kRunWeightOdd;
     a.scale_log2 = float(double(scale) * 1.4426950408889634);
     const hipError_t e = pa::launch_decode(a, group, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");

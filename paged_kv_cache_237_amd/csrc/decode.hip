@@ -8,8 +8,9 @@
 //
 // Work decomposition.  Every (sequence, kv head) pair is a "segment" of
 // ceil(ctx/64) tiles of 64 tokens.  All segments are laid end to end and the
-// resulting list of tiles is cut into n_waves equal runs, one per wave, so
-// every wave streams the same number of bytes whatever the length mix.  A
+// resulting list of tiles is cut into n_waves runs, one per wave, whose
+// lengths are set by the XCD the wave runs on (shorter on the slower,
+// odd-numbered XCDs), whatever the length mix.  A
 // workgroup holds the waves of one CU; the CU's waves share its bandwidth but
 // are not served evenly, so a wave that gets ahead of its slowest sibling
 // yields issue priority (s_setprio) and the CU's runs end together.
@@ -108,6 +109,63 @@ __device__ void locate(const DecodeArgs& a, int pos, int& b_out, int& before_out
   }
   b_out = a.batch;
   before_out = base;
+}
+
+// The runs.  Waves are numbered block * NW + wave-in-block, and block b runs
+// on XCD b % 8.  A wave on an even-numbered XCD weighs run_w_even, one on an
+// odd-numbered XCD run_w_odd; with W(w) the summed weight of waves 0 .. w-1
+// and S = W(n_waves), wave w streams tiles [total*W(w)/S, total*W(w+1)/S)
+// (rounded down), so run lengths follow the weights to within one tile.
+// That is used only when every run of waves 0 .. n_waves-1 holds at least one
+// tile (total * min weight >= S): the merge expects an arrival from every
+// wave between the first and the last run of a cut segment.  Otherwise (fewer
+// tiles than waves, roughly) the tiles are cut into runs of `per` =
+// ceil(total / n_waves), empty only at the end.
+struct Runs {
+  int64_t total;
+  int64_t sum;  // S
+  int n_waves, we, wo;
+  int per;      // > 0: equal runs of per tiles
+};
+
+// W(w): blocks alternate even, odd XCD, so a pair of blocks weighs NW*(we+wo).
+template <int NW>
+__device__ __forceinline__ int64_t run_weight_before(const Runs& r, int w) {
+  const int blk = w / NW, wv = w - blk * NW;
+  const int64_t s = int64_t(blk >> 1) * NW * (r.we + r.wo);
+  return (blk & 1) ? s + int64_t(NW) * r.we + int64_t(wv) * r.wo : s + int64_t(wv) * r.we;
+}
+
+template <int NW>
+__device__ __forceinline__ Runs make_runs(const DecodeArgs& a, int total) {
+  Runs r;
+  r.total = total;
+  r.n_waves = a.n_waves;
+  r.we = a.run_w_even;
+  r.wo = a.run_w_odd;
+  r.sum = run_weight_before<NW>(r, a.n_waves);
+  r.per = int64_t(total) * min(r.we, r.wo) >= r.sum ? 0 : (total + a.n_waves - 1) / a.n_waves;
+  return r;
+}
+
+template <int NW>
+__device__ __forceinline__ int run_start(const Runs& r, int w) {
+  if (r.per > 0) return int(min(int64_t(w) * r.per, r.total));
+  return w >= r.n_waves ? int(r.total) : int(r.total * run_weight_before<NW>(r, w) / r.sum);
+}
+
+// The wave whose run holds tile `tile` (< total).  Weighted runs: the largest
+// w with total*W(w)/S <= tile, i.e. W(w) <= V = ((tile+1)*S - 1) / total,
+// found by inverting W piecewise.
+template <int NW>
+__device__ __forceinline__ int wave_of(const Runs& r, int tile) {
+  if (r.per > 0) return tile / r.per;
+  const int64_t v = ((int64_t(tile) + 1) * r.sum - 1) / r.total;
+  const int64_t pair = int64_t(NW) * (r.we + r.wo);
+  const int64_t p = v / pair;
+  const int64_t rest = v - p * pair;
+  return int(rest < int64_t(NW) * r.we ? (2 * p) * NW + rest / r.we
+                                       : (2 * p + 1) * NW + (rest - int64_t(NW) * r.we) / r.wo);
 }
 
 // Partial records cross XCDs (each XCD has its own L2), so they are written
@@ -216,7 +274,7 @@ __device__ __forceinline__ void issue_v(const TileLoads& tl, uint4 (&vr)[16]) {
 // partial record at seg + wave.  Returns the number of cut segments, whose
 // (b, g, first run, last run) are stored in pend_*.
 template <int G>
-__device__ int stream_run(const DecodeArgs& a, int pos, int end, int per, int wave, uint4* q_lds,
+__device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& runs, int wave, uint4* q_lds,
                           float* p_lds, int* prog, int wv, int (&pend_b)[2], int (&pend_g)[2],
                           int (&pend_w0)[2], int (&pend_w1)[2]) {
   constexpr int NW = GroupShape<G>::kWaves;
@@ -420,8 +478,8 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, int per, int wa
         const int start = pos - t;  // first tile of the segment in the flattened list
         pend_b[npend] = b;
         pend_g[npend] = g;
-        pend_w0[npend] = start / per;
-        pend_w1[npend] = (start + nt - 1) / per;
+        pend_w0[npend] = wave_of<NW>(runs, start);
+        pend_w1[npend] = wave_of<NW>(runs, start + nt - 1);
         ++npend;
       }
 #pragma unroll
@@ -475,9 +533,9 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   }
 
   const int total = total_tiles(a);
-  const int per = (total + a.n_waves - 1) / a.n_waves;
-  const int pos = wave * per;
-  const int end = min(pos + per, total);
+  const Runs runs = make_runs<NW>(a, total);
+  const int pos = run_start<NW>(runs, wave);
+  const int end = run_start<NW>(runs, wave + 1);
   if (pos >= end) {
     if (lane_id() == 0) prog[wv] = 1 << 30;
     return;
@@ -487,7 +545,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   // are counted once the whole run has been streamed, so the record stores
   // never stall the loads.
   int pend_b[2], pend_g[2], pend_w0[2], pend_w1[2];
-  const int npend = stream_run<G>(a, pos, end, per, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
+  const int npend = stream_run<G>(a, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
                                   pend_g, pend_w0, pend_w1);
   // a finished wave no longer holds its siblings back
   if (lane_id() == 0) prog[wv] = 1 << 30;

@@ -45,6 +45,8 @@ struct DecodeArgs {
   int hkv;
   int mbps;        // max_blocks_per_seq
   int n_waves;     // waves in the split-context grid
+  int run_w_even;  // relative run length of waves on even- / odd-numbered XCDs
+  int run_w_odd;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -77,6 +79,12 @@ struct CopyBlocksArgs {
 // Waves per CU the decode grid is sized for.  A workgroup holds the waves of
 // one CU: 8, or 4 for G = 8 (whose waves need twice the registers).
 constexpr int kDecodeWavesPerCU = 8;
+// Workgroup b of a launch runs on XCD b % 8, and the odd-numbered XCDs
+// stream about 9 % slower than the even ones under the same load (measured
+// per XCD with the hardware's realtime counter on every MI355X we ran on), so
+// their waves get runs 11/12 as long and all XCDs finish together.
+constexpr int kRunWeightEven = 12;
+constexpr int kRunWeightOdd = 11;
 __host__ __device__ constexpr int decode_group_waves(int g) { return g == 8 ? 4 : 8; }
 
 // Records a status and its detail string for pa_last_error_detail (thread
