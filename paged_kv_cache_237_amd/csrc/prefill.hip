@@ -18,8 +18,12 @@
 //                 sum are in-lane plus one exchange with lane^32.
 //   O  = P V    : A = bf16(P) taken straight from the S^T accumulator -- the
 //                 contraction runs over keys in the accumulator's register
-//                 order, and V is read from a transposed LDS copy ([dim][key])
-//                 in that same key order, so P never moves between lanes.
+//                 order (per 16 keys, lane half h holds keys 4h..4h+3 and
+//                 8+4h..8+4h+3), and V is kept in LDS transposed ([dim][key])
+//                 with each 16 keys stored in the order 0-3, 8-11, 4-7,
+//                 12-15, so a lane's 8 keys of one MFMA are one 16-byte read
+//                 and P never moves between lanes.  The transposed tile is
+//                 written with 8-byte stores (4 keys of one dim each).
 // Online softmax in the log2 domain (scale*log2 e folded into one FMA) with a
 // lazy rescale: the reference max only moves when a row's max grows by more
 // than 2^8, so O is rescaled rarely.  Tiles entirely above a wave's diagonal
@@ -39,7 +43,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerWG = 128;  // query rows (head, position) per workgroup: 32 per wave
 constexpr int kKeys = 64;        // keys per K/V tile
-constexpr int kVtStride = 68;    // bf16 per transposed-V row in LDS (64 keys + pad)
+constexpr int kVtStride = 72;    // bf16 per transposed-V row in LDS (64 keys + pad, 16-B aligned)
 constexpr float kLazyRescale = 8.f;  // log2 headroom before O is rescaled
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
@@ -90,18 +94,14 @@ __device__ __forceinline__ void load_k(const PrefillArgs& a, const int32_t* tabl
   }
 }
 
-// V tile t -> registers: 2 chunks of 2 consecutive keys per thread.
+// V tile t -> registers: 4 consecutive keys of one 8-dim chunk per thread.
 __device__ __forceinline__ void load_v(const PrefillArgs& a, const int32_t* table, int g, int ctx,
-                                       int t, int tid, uint4 (&va)[2], uint4 (&vb)[2]) {
+                                       int t, int tid, uint4 (&vr)[4]) {
   const TileGeom tg = tile_geom(a, table, g, ctx, t);
-  const int kp = tid & 31;  // key pair
+  const int kq = tid & 15, ch = tid >> 4;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ch = (tid >> 5) + 8 * j;
-    const uint32_t off = uint32_t((tg.r0 + 2 * kp) * kChunks + ch) * 16u;
-    va[j] = buf_load16(tg.rv, off, 0u);
-    vb[j] = buf_load16(tg.rv, off + 256u, 0u);
-  }
+  for (int i = 0; i < 4; ++i)
+    vr[i] = buf_load16(tg.rv, uint32_t((tg.r0 + 4 * kq + i) * kChunks + ch) * 16u, 0u);
 }
 
 __device__ __forceinline__ void store_k(uint4* kbuf, int tid, const uint4 (&kx)[4]) {
@@ -110,22 +110,27 @@ __device__ __forceinline__ void store_k(uint4* kbuf, int tid, const uint4 (&kx)[
   for (int j = 0; j < 4; ++j) kdst[256 * j] = kx[j];
 }
 
-// V transposed to [dim][key], pairs of keys per dword; every address is a
-// per-thread base plus a compile-time offset.
-__device__ __forceinline__ void store_v(uint16_t* vtbuf, int tid, const uint4 (&va)[2],
-                                        const uint4 (&vb)[2]) {
-  // thread (kp = tid%32, ch = tid/32 (+8)): dims 8*ch .. 8*ch+7, keys 2kp, 2kp+1
-  uint32_t* vdst = reinterpret_cast<uint32_t*>(vtbuf) + ((tid >> 5) * 8 * kVtStride) / 2 + (tid & 31);
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
+  return i == 0 ? u.x : (i == 1 ? u.y : (i == 2 ? u.z : u.w));
+}
+
+// V transposed to [dim][key]: each thread writes its 4 keys of each of its 8
+// dims as one 8-byte store.  Within 16 keys the order is the one the PV
+// operand reads (0-3, 8-11, 4-7, 12-15), so a lane's 8 keys of one k-step are
+// one 16-byte read.
+__device__ __forceinline__ void store_v(uint16_t* vtbuf, int tid, const uint4 (&vr)[4]) {
+  const int kq = tid & 15, ch = tid >> 4;
+  const int q = kq & 3;
+  const int pos = 16 * (kq >> 2) + 4 * (((q & 1) << 1) | (q >> 1));
+  uint2* base = reinterpret_cast<uint2*>(vtbuf + 8 * ch * kVtStride + pos);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t r0w[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
-    const uint32_t r1w[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 64 * j + 2 * e;  // dim offset from this thread's first dim
-      vdst[(d * kVtStride) / 2] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x05040100u);
-      vdst[((d + 1) * kVtStride) / 2] = __builtin_amdgcn_perm(r1w[e], r0w[e], 0x07060302u);
-    }
+  for (int e2 = 0; e2 < 4; ++e2) {  // dims 2*e2, 2*e2+1 of the chunk
+    const uint32_t a0 = word_of(vr[0], e2), a1 = word_of(vr[1], e2);
+    const uint32_t a2 = word_of(vr[2], e2), a3 = word_of(vr[3], e2);
+    base[(2 * e2) * (kVtStride / 4)] =
+        make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u));
+    base[(2 * e2 + 1) * (kVtStride / 4)] =
+        make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u));
   }
 }
 
@@ -189,10 +194,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   // Tile t+1 is loaded into registers while tile t is computed from LDS;
   // the two LDS buffers alternate.
-  uint4 kx[4], va[2], vb[2];
+  uint4 kx[4], vr[4];
   if (ntiles > 0) {
     load_k(a, table, g, ctx, 0, tid, kx);
-    load_v(a, table, g, ctx, 0, tid, va, vb);
+    load_v(a, table, g, ctx, 0, tid, vr);
   }
 
   const float c = a.scale_log2;
@@ -284,16 +289,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
 
     // O += P V; lane reads dims 32n + col, keys 16ks + 4*half + {0..3, 8..11}
-    const uint32_t* vsrc =
-        reinterpret_cast<const uint32_t*>(sm.vt[t & 1]) + (col * kVtStride + 4 * half) / 2;
+    const uint16_t* vsrc = sm.vt[t & 1] + col * kVtStride + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int off = (32 * n * kVtStride + 16 * ks) / 2;  // in dwords, compile-time
-        const uint2 lo = *reinterpret_cast<const uint2*>(vsrc + off);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vsrc + off + 4);
-        const bf16x8_t vop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const int off = 32 * n * kVtStride + 16 * ks;  // bf16, compile-time
+        const bf16x8_t vop = as_bf16x8(*reinterpret_cast<const uint4*>(vsrc + off));
         o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], vop, o[n], 0, 0, 0);
       }
     }
@@ -303,10 +305,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // Buffer t&1 last held tile t-2, which every wave finished computing
     // before the previous barrier.
     store_k(sm.k[t & 1], tid, kx);
-    store_v(sm.vt[t & 1], tid, va, vb);
+    store_v(sm.vt[t & 1], tid, vr);
     if (t + 1 < ntiles) {
       load_k(a, table, g, ctx, t + 1, tid, kx);
-      load_v(a, table, g, ctx, t + 1, tid, va, vb);
+      load_v(a, table, g, ctx, t + 1, tid, vr);
     }
     __syncthreads();
     if (t * kKeys > amax) continue;  // every key of the tile is above this wave's diagonal
