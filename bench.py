@@ -162,6 +162,8 @@ def time_prefill(case: wl.PagedCase, steps: int, warmup: int):
     out = torch.empty((case.total_q_rows, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
                       device="cuda")
     stream = torch.cuda.current_stream()
+    ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len, case.num_q_heads,
+                                    case.num_kv_heads, case.max_blocks_per_seq)
 
     def step(ev=None):
         if ev is not None:
@@ -170,7 +172,7 @@ def time_prefill(case: wl.PagedCase, steps: int, warmup: int):
         if ev is not None:
             ev[1].record(stream)
         pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache,
-                   dev.v_cache, dev.block_table, case.scale)
+                   dev.v_cache, dev.block_table, case.scale, ws)
         if ev is not None:
             ev[2].record(stream)
 
@@ -557,7 +559,7 @@ def main(argv=None):
                            "sum_context_len": int(c.context_lens.sum())}
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(10, args.steps // 5), 3)
-        for name in ("chunked_prefill_mixed", "multi_query_decode"):
+        for name in ("chunked_prefill_mixed", "multi_query_decode", "long_prefix_chunk"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(10, args.steps // 5), 3)
         print("[bench] extra block copy / swap", file=sys.stderr, flush=True)

@@ -143,12 +143,12 @@ size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_
  *                   (must be <= max_blocks_per_seq*block_size).
  *   scale         : the logit scale (e.g. 1/sqrt(head_dim)); finite.
  *   workspace     : >= pa_decode_workspace_size(...) bytes of device memory,
- *                   256-B aligned.  It must be ZERO-FILLED before its first
- *                   use; every call leaves it zero-filled again (it holds one
- *                   arrival counter per (sequence, kv head) that the last
- *                   contributing wave resets, plus partial results that are
- *                   scratch).  Calls that overlap in time must not share a
- *                   workspace.
+ *                   256-B aligned.  It holds one arrival counter per
+ *                   (sequence, kv head), which must be zero before the first
+ *                   call (zero-fill the whole workspace once) and which every
+ *                   call resets to zero, plus partial results that are scratch
+ *                   and need no clearing.  Calls that overlap in time must not
+ *                   share a workspace.
  *   Source: CSDN essay, first and third sections; vLLM decode kernel
  *   description in the same essay.
  */
@@ -160,6 +160,16 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * pa_prefill_workspace_size -- bytes of device workspace pa_prefill needs for
+ * these sizes (0 when no query block can be split: contexts of at most
+ * 2048 tokens, i.e. max_blocks_per_seq <= 8).  Also 0 for invalid arguments;
+ * pa_prefill then reports the error.
+ */
+size_t pa_prefill_workspace_size(int32_t batch, int64_t total_q_rows, int32_t max_seqlen_q,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq);
+
+/*
  * pa_prefill -- causal varlen attention of prompt tokens over the paged cache.
  *
  * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (q_len_b of
@@ -169,20 +179,28 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * seen in full), with the same softmax formula as pa_decode.  The K/V of all
  * context_lens[b] positions must already be in the cache.
  *
- *   out, q        : bf16 [total_q][num_q_heads][head_dim], 16-B aligned,
- *                   total_q = cu_seqlens_q[batch].
- *   cu_seqlens_q  : int32 [batch+1], non-decreasing, cu_seqlens_q[0] = 0.
+ *   out, q        : bf16 [total_q_rows][num_q_heads][head_dim], 16-B aligned.
+ *   cu_seqlens_q  : int32 [batch+1], non-decreasing, cu_seqlens_q[0] = 0,
+ *                   cu_seqlens_q[batch] = total_q_rows (if it is larger, no
+ *                   query block is split, which is slower but still correct).
  *   context_lens  : int32 [batch].
  *   max_seqlen_q  : an upper bound of q_len_b (sizes the launch).
+ *   workspace     : DEVICE, 256-B aligned, at least pa_prefill_workspace_size
+ *                   bytes (may be NULL when that is 0): scratch for the
+ *                   partial states of query blocks whose context is split
+ *                   across workgroups (a second kernel on the same stream
+ *                   merges them).  No initial contents are needed.  Calls
+ *                   that overlap in time must not share a workspace.
  *   Source: nano-vllm hub page, "Scheduler" (prefill fills the cache with the
- *   prompt); CSDN essay, reading vLLM's attention module (prefill kernel).
+ *   prompt); CSDN essay, reading vLLM's attention module (prefill kernel);
+ *   the split-context merge follows the decode description in the same essay.
  */
 int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
                const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
-               const void* k_cache, const void* v_cache, const int32_t* block_table,
-               int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
-               int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-               void* stream);
+               int64_t total_q_rows, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+               float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_copy_blocks -- copy whole cache blocks inside one pool (copy-on-write of

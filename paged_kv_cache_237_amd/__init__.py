@@ -33,7 +33,8 @@ STATUS_NAMES = {
     -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT", -10: "PA_ERR_NO_BLOCKS",
 }
 
-EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_prefill",
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_prefill_workspace_size",
+           "pa_prefill",
            "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append",
            "pa_bm_append_batch", "pa_bm_fork", "pa_bm_free", "pa_bm_seq_len", "pa_bm_block_table", "pa_bm_slot_mapping",
@@ -72,8 +73,10 @@ def lib() -> ctypes.CDLL:
         l.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_decode.restype = ctypes.c_int
-        l.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
-                                 _i32, _i32, _i64, _f32, _vp]
+        l.pa_prefill_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
+        l.pa_prefill_workspace_size.restype = _sz
+        l.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _i32,
+                                 _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_prefill.restype = ctypes.c_int
         l.pa_status_string.argtypes = [ctypes.c_int]
         l.pa_status_string.restype = ctypes.c_char_p
@@ -186,8 +189,8 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int) -> in
 
 
 def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, device="cuda"):
-    """A zero-filled decode workspace (pa_decode leaves it zero-filled, so it
-    can be reused by later calls of the same or a smaller shape)."""
+    """A zero-filled decode workspace (pa_decode resets its counters to zero,
+    so it can be reused by later calls of the same or a smaller shape)."""
     n = decode_workspace_size(batch, num_q_heads, num_kv_heads)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
@@ -211,10 +214,26 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_len:
         workspace.numel() * workspace.element_size(), _stream(q, stream)))
 
 
+def prefill_workspace_size(batch: int, total_q_rows: int, max_seqlen_q: int, num_q_heads: int,
+                           num_kv_heads: int, max_blocks_per_seq: int) -> int:
+    return int(lib().pa_prefill_workspace_size(batch, total_q_rows, max_seqlen_q, num_q_heads,
+                                               num_kv_heads, HEAD_DIM, BLOCK_SIZE, max_blocks_per_seq))
+
+
+def alloc_prefill_workspace(batch: int, total_q_rows: int, max_seqlen_q: int, num_q_heads: int,
+                            num_kv_heads: int, max_blocks_per_seq: int, device="cuda"):
+    """A prefill workspace (scratch: no initial contents needed), or None
+    when these sizes need none."""
+    n = prefill_workspace_size(batch, total_q_rows, max_seqlen_q, num_q_heads, num_kv_heads,
+                               max_blocks_per_seq)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
 def prefill(out, q, cu_seqlens_q, context_lens, max_seqlen_q: int, k_cache, v_cache,
-            block_table, scale: float, stream=None) -> None:
-    """pa_prefill: q/out [total_q, Hq, 128], cu_seqlens_q int32 [B+1],
-    context_lens int32 [B], block_table int32 [B, max_blocks_per_seq]."""
+            block_table, scale: float, workspace=None, stream=None) -> None:
+    """pa_prefill: q/out [total_q, Hq, 128], cu_seqlens_q int32 [B+1] with
+    cu_seqlens_q[B] = total_q, context_lens int32 [B], block_table int32
+    [B, max_blocks_per_seq]; workspace from alloc_prefill_workspace."""
     nb, hkv = _cache_geometry(k_cache, v_cache)
     tq, hq, d = (int(x) for x in q.shape)
     b = int(context_lens.shape[0])
@@ -222,12 +241,16 @@ def prefill(out, q, cu_seqlens_q, context_lens, max_seqlen_q: int, k_cache, v_ca
         raise ValueError("shape mismatch between q, out, cu_seqlens_q and context_lens")
     if block_table.dim() != 2 or block_table.shape[0] != b:
         raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", (torch.uint8, torch.float32, torch.int32))
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().pa_prefill(
         _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(cu_seqlens_q, "cu_seqlens_q", _I32),
-        _dev(context_lens, "context_lens", _I32), b, int(max_seqlen_q),
+        _dev(context_lens, "context_lens", _I32), b, int(max_seqlen_q), tq,
         _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
         _dev(block_table, "block_table", _I32), int(block_table.shape[1]), hq, hkv, d,
-        BLOCK_SIZE, nb, float(scale), _stream(q, stream)))
+        BLOCK_SIZE, nb, float(scale), ws_ptr, ws_bytes, _stream(q, stream)))
 
 
 def validate_slots(slots_host, num_slots: int) -> int:

@@ -105,6 +105,44 @@ size_t decode_ws_bytes(int32_t batch, int32_t num_kv_heads, int group, int64_t w
   return decode_counter_bytes(batch, num_kv_heads) + ((bytes + 255) & ~size_t(255));
 }
 
+// Prefill context split: parts per query block and tiles per part.  Only a
+// launch with fewer query blocks than workgroup slots (2 per CU; the
+// 256-CU gfx950 part is assumed, so that the workspace size does not depend
+// on which device is current -- the split only affects speed) can leave CUs
+// idle while a few blocks stream long contexts; only then are blocks split,
+// into enough parts for about four workgroups per slot (every other launch
+// gets max_splits = 1: no records, no merge, no empty workgroups).
+struct PrefillSplit {
+  int split_tiles, max_splits, nqb_max;
+  size_t ml_bytes, o_bytes;
+};
+
+constexpr int64_t kPrefillSlots = 2 * 256;
+
+PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seqlen_q,
+                           int32_t num_q_heads, int32_t num_kv_heads, int group,
+                           int32_t max_blocks_per_seq) {
+  PrefillSplit ps;
+  const int64_t max_tiles = int64_t(max_blocks_per_seq) * (PA_BLOCK_SIZE / pa::kTile);
+  ps.split_tiles = int(std::max<int64_t>(pa::kPrefillSplitTiles,
+                                         (max_tiles + pa::kPrefillMaxSplits - 1) / pa::kPrefillMaxSplits));
+  const int qb = pa::kPrefillRows / group;
+  ps.nqb_max = (max_seqlen_q + qb - 1) / qb;
+  const int64_t slots = kPrefillSlots;
+  const int64_t blocks = std::max<int64_t>(1, int64_t(batch) * num_kv_heads * ps.nqb_max);
+  const int64_t want = blocks >= slots ? 1 : (4 * slots + blocks - 1) / blocks;
+  ps.max_splits = int(std::max<int64_t>(
+      1, std::min<int64_t>(want, (max_tiles + ps.split_tiles - 1) / ps.split_tiles)));
+  if (ps.max_splits == 1) {
+    ps.ml_bytes = ps.o_bytes = 0;
+    return ps;
+  }
+  const size_t rows = size_t(ps.max_splits) * size_t(std::max<int64_t>(total_q_rows, 0)) * size_t(num_q_heads);
+  ps.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+  ps.o_bytes = rows * size_t(pa::kDim) * sizeof(float);
+  return ps;
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,14 +414,30 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   }
 }
 
+size_t pa_prefill_workspace_size(int32_t batch, int64_t total_q_rows, int32_t max_seqlen_q,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq) {
+  try {
+    int group = 0;
+    if (batch < 0 || total_q_rows < 0 || max_seqlen_q < 0 || max_blocks_per_seq <= 0) return 0;
+    if (check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group) != PA_OK) return 0;
+    const PrefillSplit ps = prefill_split(batch, total_q_rows, max_seqlen_q, num_q_heads,
+                                          num_kv_heads, group, max_blocks_per_seq);
+    return ps.ml_bytes + ps.o_bytes;
+  } catch (...) {
+    return 0;
+  }
+}
+
 int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
                const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
-               const void* k_cache, const void* v_cache, const int32_t* block_table,
-               int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
-               int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-               void* stream) {
+               int64_t total_q_rows, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+               float scale, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
+    if (total_q_rows < 0) return fail(PA_ERR_BAD_SHAPE, "total_q_rows < 0");
     int group = 0;
     int r = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group);
     if (r != PA_OK) return r;
@@ -392,9 +446,21 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
     if (max_seqlen_q < 0 || int64_t(max_seqlen_q) > int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE)
       return fail(PA_ERR_BAD_SHAPE, "max_seqlen_q outside [0, max_blocks_per_seq*block_size]");
     if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
-    if (batch == 0 || max_seqlen_q == 0) return ok();
+    if (batch == 0 || max_seqlen_q == 0 || total_q_rows == 0) return ok();
     if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_table)
       return fail(PA_ERR_NULL_PTR, "pa_prefill: a pointer argument is NULL");
+    const PrefillSplit ps = prefill_split(batch, total_q_rows, max_seqlen_q, num_q_heads,
+                                          num_kv_heads, group, max_blocks_per_seq);
+    const size_t need = ps.ml_bytes + ps.o_bytes;
+    if (need > 0) {
+      if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
+      if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
+      if (workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                          std::to_string(workspace_bytes));
+    }
+    if (int64_t(batch) * ps.max_splits > int64_t(INT32_MAX) || 2 * int64_t(ps.nqb_max) > 65535)
+      return fail(PA_ERR_BAD_SHAPE, "launch grid too large");
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))
       return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, int32 arrays 4-byte");
@@ -413,6 +479,12 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
     a.mbps = max_blocks_per_seq;
     a.max_q = max_seqlen_q;
     a.scale_log2 = float(double(scale) * 1.4426950408889634);
+    a.split_tiles = ps.split_tiles;
+    a.max_splits = ps.max_splits;
+    a.total_q = total_q_rows;
+    char* wsb = static_cast<char*>(workspace);
+    a.rec_ml = need > 0 ? reinterpret_cast<float*>(wsb) : nullptr;
+    a.rec_o = need > 0 ? reinterpret_cast<float*>(wsb + ps.ml_bytes) : nullptr;
     const hipError_t e = pa::launch_prefill(a, group, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available");
     if (e != hipSuccess) return hip_fail(e, "prefill launch");

@@ -65,7 +65,19 @@ struct PrefillArgs {
   int mbps;
   int max_q;
   float scale_log2;
+  // context split (see prefill.hip): a query block of more than split_tiles
+  // key tiles is cut into up to max_splits parts merged through the records
+  int split_tiles;
+  int max_splits;
+  int64_t total_q;   // rows the records are sized for
+  float* rec_ml;     // [max_splits][total_q][hq][2] (m, l)
+  float* rec_o;      // [max_splits][total_q][hq][kDim] unnormalised outputs
 };
+
+// Query rows per prefill workgroup, key tiles per split part, parts per block.
+constexpr int kPrefillRows = 128;
+constexpr int kPrefillSplitTiles = 32;
+constexpr int kPrefillMaxSplits = 16;
 
 struct CopyBlocksArgs {
   const int32_t* pairs;  // [n_pairs][2] (src, dst)

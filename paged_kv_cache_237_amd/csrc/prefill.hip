@@ -31,6 +31,17 @@
 // loaded as zeros through raw-buffer range checks (the cache may hold NaN
 // patterns there).  Workgroups are dispatched longest-first: grid z counts
 // query blocks from the end of each sequence.
+//
+// Context split: a query block whose keys span more than split_tiles tiles
+// (a long cached prefix) is cut into nsplit = ceil(tiles / split_tiles) key
+// ranges of near-equal length, one workgroup each, so that no workgroup
+// streams a very long context alone (grid x = sequence * max_splits + part).
+// Each part leaves its rows' unnormalised state (m, l, O) in the workspace
+// records, and a second, small kernel on the same stream merges them:
+// M = max m_i, L = sum 2^(m_i - M) l_i, o = sum 2^(m_i - M) O_i / L (the same
+// split-context identity as decode), taken part by part with an online
+// rescale.  The kernel boundary makes the records visible, so both sides use
+// ordinary cached accesses.
 #include <math.h>
 
 #include "pa_device.hpp"
@@ -41,7 +52,7 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kRowsPerWG = 128;  // query rows (head, position) per workgroup: 32 per wave
+constexpr int kRowsPerWG = kPrefillRows;  // query rows (head, position) per workgroup: 32 per wave
 constexpr int kKeys = 64;        // keys per K/V tile
 constexpr int kVtStride = 72;    // bf16 per transposed-V row in LDS (64 keys + pad, 16-B aligned)
 constexpr float kLazyRescale = 8.f;  // log2 headroom before O is rescaled
@@ -134,6 +145,127 @@ __device__ __forceinline__ void store_v(uint16_t* vtbuf, int tid, const uint4 (&
   }
 }
 
+// Geometry of query block jrev (counted from the end) of sequence b, shared
+// by the attention and merge kernels so that both agree on every split.
+template <int G>
+struct BlockGeom {
+  int q0, qlen, ctx, nqb, p0, shift, ntiles, nsplit;
+
+  __device__ __forceinline__ BlockGeom(const PrefillArgs& a, int b, int jrev) {
+    constexpr int QB = kRowsPerWG / G;
+    q0 = a.cu_q[b];
+    qlen = max(0, a.cu_q[b + 1] - q0);
+    ctx = min(max(a.ctx_lens[b], 0), a.mbps * kBlock);
+    nqb = (qlen + QB - 1) / QB;
+    p0 = (nqb - 1 - jrev) * QB;
+    shift = ctx - qlen;  // absolute position of query row 0
+    // keys the whole block needs
+    const int last_row = min(p0 + QB, qlen) - 1;
+    const int kend = min(shift + last_row + 1, ctx);
+    ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+    // records exist only when they are sized for every row
+    nsplit = min(max((ntiles + a.split_tiles - 1) / a.split_tiles, 1), a.max_splits);
+    if (nsplit > 1 && int64_t(a.cu_q[a.batch]) > a.total_q) nsplit = 1;
+  }
+};
+
+// One part of a split query block: its rows' (m, l, O) to the records.
+template <int G>
+__device__ void write_part(const PrefillArgs& a, int g, int part, int q0, int qlen, int p0,
+                           const f32x16_t (&o)[4], float m, float ltot) {
+  constexpr int QB = kRowsPerWG / G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int64_t pbase = int64_t(part) * a.total_q * a.hq;  // first record row of this part
+  auto rec_row = [&](int R) -> int64_t {
+    return pbase + (int64_t(q0) + p0 + R % QB) * a.hq + g * G + R / QB;
+  };
+  // (m, l): lane (col, half 0) owns row w*32 + col
+  {
+    const int R = w * 32 + col;
+    if (half == 0 && p0 + R % QB < qlen)
+      *reinterpret_cast<float2*>(a.rec_ml + rec_row(R) * 2) = make_float2(m, ltot);
+  }
+  // O: register 4*qd + i of o[n] is row 8*qd + 4*half + i of the wave, dim 32*n + col
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int R = w * 32 + 8 * qd + 4 * half + i;
+      if (p0 + R % QB < qlen) {
+        float* ro = a.rec_o + rec_row(R) * kDim + col;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) ro[32 * n] = o[n][4 * qd + i];
+      }
+    }
+}
+
+// Merge of split query blocks: workgroup (b, g, z) takes rows 64*(z&1) ..
+// +63 of block z/2; thread (r8, d4) rows r8 + 8i (i < 8), dims 4*d4 .. +3.
+// All loads of one part for the thread's 8 rows are independent and issued
+// together; parts are folded in with an online rescale.
+template <int G>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+  constexpr int QB = kRowsPerWG / G;
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int jrev = blockIdx.z >> 1, rhalf = blockIdx.z & 1;
+  const BlockGeom<G> bg(a, b, jrev);
+  if (jrev >= bg.nqb || bg.nsplit <= 1) return;
+  const int r8 = threadIdx.x >> 5, d4 = threadIdx.x & 31;
+  const int64_t pstride = a.total_q * a.hq;
+  int64_t rr[8];
+  bool ok[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int R = 64 * rhalf + r8 + 8 * i;
+    ok[i] = bg.p0 + R % QB < bg.qlen;
+    rr[i] = (int64_t(bg.q0) + bg.p0 + R % QB) * a.hq + g * G + R / QB;
+  }
+  float M[8], L[8], acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    M[i] = -INFINITY;
+    L[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+  }
+  for (int s = 0; s < bg.nsplit; ++s) {
+    float2 ml[8];
+    float4 u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = s * pstride + (ok[i] ? rr[i] : 0);
+      ml[i] = *reinterpret_cast<const float2*>(a.rec_ml + r * 2);
+      u[i] = *reinterpret_cast<const float4*>(a.rec_o + r * kDim + 4 * d4);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float mn = fmaxf(M[i], ml[i].x);
+      if (mn == -INFINITY) continue;  // no visible key in any part so far
+      const float fo = __builtin_amdgcn_exp2f(M[i] - mn);  // 0 while M is -inf
+      const float fs = __builtin_amdgcn_exp2f(ml[i].x - mn);
+      L[i] = L[i] * fo + ml[i].y * fs;
+      acc[i][0] = acc[i][0] * fo + u[i].x * fs;
+      acc[i][1] = acc[i][1] * fo + u[i].y * fs;
+      acc[i][2] = acc[i][2] * fo + u[i].z * fs;
+      acc[i][3] = acc[i][3] * fo + u[i].w * fs;
+      M[i] = mn;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (!ok[i]) continue;
+    const float inv = L[i] > 0.f ? 1.f / L[i] : 0.f;
+    // record row (q row, head) = output row
+    uint2* dst = reinterpret_cast<uint2*>(a.out + rr[i] * kDim + 4 * d4);
+    *dst = make_uint2(pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv),
+                      pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv));
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int QB = kRowsPerWG / G;  // positions per workgroup
@@ -141,7 +273,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   PrefillLds& sm = *reinterpret_cast<PrefillLds*>(lds_raw);
   float (*rowf)[32] = sm.rowf;
 
-  const int b = blockIdx.x;
+  const int b = blockIdx.x / a.max_splits;
+  const int part = blockIdx.x - b * a.max_splits;
   const int g = blockIdx.y;
   const int jrev = blockIdx.z;
   const int tid = threadIdx.x;
@@ -150,14 +283,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  const int q0 = a.cu_q[b];
-  const int qlen = max(0, a.cu_q[b + 1] - q0);
-  const int cap = a.mbps * kBlock;
-  const int ctx = min(max(a.ctx_lens[b], 0), cap);
-  const int nqb = (qlen + QB - 1) / QB;
-  if (jrev >= nqb) return;
-  const int p0 = (nqb - 1 - jrev) * QB;
-  const int shift = ctx - qlen;  // absolute position of query row 0
+  const BlockGeom<G> bg(a, b, jrev);
+  if (jrev >= bg.nqb) return;
+  const int q0 = bg.q0, qlen = bg.qlen, ctx = bg.ctx, p0 = bg.p0, shift = bg.shift;
+  const int ntiles = bg.ntiles, nsplit = bg.nsplit;
 
   // This lane's query row (the S^T column it owns): head hl, position pos.
   const int R = w * 32 + col;
@@ -177,11 +306,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   amax = __builtin_amdgcn_readfirstlane(amax);
   amin = __builtin_amdgcn_readfirstlane(amin);
 
-  // Keys the whole workgroup needs.
-  const int last_row = min(p0 + QB, qlen) - 1;
-  const int kend = min(shift + last_row + 1, ctx);
-  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
   const int32_t* table = a.block_table + int64_t(b) * a.mbps;
+
+  // This part's key tiles [t_begin, t_end).
+  if (part >= nsplit) return;
+  const int t_begin = int(int64_t(ntiles) * part / nsplit);
+  const int t_end = int(int64_t(ntiles) * (part + 1) / nsplit);
 
   // Q^T operand: dims 16*ks + 8*half .. +7 of the lane's row, 8 k-steps.
   bf16x8_t qop[8];
@@ -195,9 +325,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // Tile t+1 is loaded into registers while tile t is computed from LDS;
   // the two LDS buffers alternate.
   uint4 kx[4], vr[4];
-  if (ntiles > 0) {
-    load_k(a, table, g, ctx, 0, tid, kx);
-    load_v(a, table, g, ctx, 0, tid, vr);
+  if (t_begin < t_end) {
+    load_k(a, table, g, ctx, t_begin, tid, kx);
+    load_v(a, table, g, ctx, t_begin, tid, vr);
   }
 
   const float c = a.scale_log2;
@@ -301,12 +431,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_begin; t < t_end; ++t) {
     // Buffer t&1 last held tile t-2, which every wave finished computing
     // before the previous barrier.
     store_k(sm.k[t & 1], tid, kx);
     store_v(sm.vt[t & 1], tid, vr);
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_end) {
       load_k(a, table, g, ctx, t + 1, tid, kx);
       load_v(a, table, g, ctx, t + 1, tid, vr);
     }
@@ -317,9 +447,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     softmax_pv(t, s);
   }
 
+  const float ltot = l + __shfl_xor(l, 32, 64);
+  if (nsplit > 1) {
+    write_part<G>(a, g, part, q0, qlen, p0, o, m, ltot);
+    return;
+  }
+
   // ---- epilogue: O / l -> bf16, staged through LDS for 16-byte stores -------
   __syncthreads();  // tile buffers are reused below
-  const float ltot = l + __shfl_xor(l, 32, 64);
   if (half == 0) rowf[w][col] = ltot > 0.f ? 1.f / ltot : 0.f;
   __builtin_amdgcn_wave_barrier();
   uint16_t* stage = reinterpret_cast<uint16_t*>(lds_raw) + w * (32 * kDim);  // [32 rows][128]
@@ -364,8 +499,14 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
       int(kPrefillLds));
   if (attr != hipSuccess) return attr;
   const int nqb = (a.max_q + QB - 1) / QB;
-  const dim3 grid(unsigned(a.batch), unsigned(a.hkv), unsigned(nqb));
+  const dim3 grid(unsigned(a.batch) * unsigned(a.max_splits), unsigned(a.hkv), unsigned(nqb));
   hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), kPrefillLds, s, a);
+  if (a.max_splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_merge_kernel<G>, dim3(unsigned(a.batch), unsigned(a.hkv), unsigned(2 * nqb)),
+                       dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -49,6 +49,15 @@ def test_status_strings():
 FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced on these paths
 
 
+def no_launch(status):
+    """The calls below use fake pointers, so each must fail a host check or
+    return before launching anything.  A call that passed every check would
+    launch on them -- on a machine without a GPU that launch fails with
+    PA_ERR_HIP, which is therefore a test error here."""
+    assert status != -6, "the call reached the GPU launch with fake pointers"
+    return status
+
+
 @needs_lib
 def test_store_rejects_bad_arguments_on_the_host():
     lib = pa.lib()
@@ -56,8 +65,8 @@ def test_store_rejects_bad_arguments_on_the_host():
 
     def call(**kw):
         a = {**args, **kw}
-        return lib.pa_store_kv(a["k"], a["v"], a["s"], a["n"], a["kc"], a["vc"], a["nb"], a["bs"],
-                               a["hkv"], a["d"], None)
+        return no_launch(lib.pa_store_kv(a["k"], a["v"], a["s"], a["n"], a["kc"], a["vc"], a["nb"], a["bs"],
+                               a["hkv"], a["d"], None))
 
     assert call(n=0) == 0                      # empty batch: no-op
     assert call(n=-1) == -2
@@ -80,9 +89,9 @@ def test_decode_rejects_bad_arguments_on_the_host():
 
     def call(**kw):
         a = {**base, **kw}
-        return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"], a["cl"],
+        return no_launch(lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"], a["cl"],
                              a["b"], a["maxc"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
-                             a["scale"], a["ws"], a["wsb"], None)
+                             a["scale"], a["ws"], a["wsb"], None))
 
     assert call(b=0) == 0
     assert call(b=-1) == -2
@@ -103,15 +112,18 @@ def test_decode_rejects_bad_arguments_on_the_host():
 
 @needs_lib
 def test_prefill_rejects_bad_arguments_on_the_host():
+    """Every call below either fails a host check or returns before the
+    launch (an empty batch or no query rows): the pointers are fake, so a
+    call that passed every check would launch a kernel on them."""
     lib = pa.lib()
-    base = dict(out=FAKE, q=FAKE, cu=FAKE, cl=FAKE, b=2, maxq=100, kc=FAKE, vc=FAKE, bt=FAKE,
-                mbps=4, hq=16, hkv=8, d=128, bs=256, nb=8, scale=0.088)
+    base = dict(out=FAKE, q=FAKE, cu=FAKE, cl=FAKE, b=2, maxq=100, tq=150, kc=FAKE, vc=FAKE,
+                bt=FAKE, mbps=4, hq=16, hkv=8, d=128, bs=256, nb=8, scale=0.088, ws=None, wsb=0)
 
     def call(**kw):
         a = {**base, **kw}
-        return lib.pa_prefill(a["out"], a["q"], a["cu"], a["cl"], a["b"], a["maxq"], a["kc"],
-                              a["vc"], a["bt"], a["mbps"], a["hq"], a["hkv"], a["d"], a["bs"],
-                              a["nb"], a["scale"], None)
+        return no_launch(lib.pa_prefill(a["out"], a["q"], a["cu"], a["cl"], a["b"], a["maxq"], a["tq"],
+                              a["kc"], a["vc"], a["bt"], a["mbps"], a["hq"], a["hkv"], a["d"],
+                              a["bs"], a["nb"], a["scale"], a["ws"], a["wsb"], None))
 
     assert call(b=0) == 0
     assert call(maxq=0) == 0
@@ -122,6 +134,19 @@ def test_prefill_rejects_bad_arguments_on_the_host():
     assert call(cu=None) == -1
     assert call(q=FAKE + 4) == -4
     assert call(scale=float("inf")) == -2
+    assert call(tq=-1) == -2
+    assert call(tq=0) == 0
+    # contexts of up to 2048 tokens (8 blocks) are never split: no workspace
+    # (not called here: with valid arguments the call would launch on the
+    # fake pointers)
+    assert lib.pa_prefill_workspace_size(2, 150, 100, 16, 8, 128, 256, 8) == 0
+    # longer ones may be: the workspace is then required, aligned and large enough
+    need = lib.pa_prefill_workspace_size(2, 150, 100, 16, 8, 128, 256, 40)
+    assert need > 0
+    assert call(mbps=40, maxq=100) == -5
+    assert call(mbps=40, ws=FAKE + 16, wsb=need) == -4
+    assert call(mbps=40, ws=FAKE, wsb=need - 1) == -5
+    assert lib.pa_prefill_workspace_size(2, 150, 100, 20, 8, 128, 256, 40) == 0  # bad heads
 
 
 @needs_lib
@@ -140,8 +165,8 @@ def test_copy_blocks_rejects_bad_arguments_on_the_host():
 
     def call(**kw):
         a = {**base, **kw}
-        return lib.pa_copy_blocks(a["kc"], a["vc"], a["p"], a["n"], a["nb"], a["bs"], a["hkv"],
-                                  a["d"], None)
+        return no_launch(lib.pa_copy_blocks(a["kc"], a["vc"], a["p"], a["n"], a["nb"], a["bs"], a["hkv"],
+                                  a["d"], None))
 
     assert call(n=0) == 0
     assert call(n=-1) == -2
@@ -164,8 +189,8 @@ def test_swap_blocks_rejects_bad_arguments_on_the_host():
 
     def call(**kw):
         a = {**base, **kw}
-        return lib.pa_swap_blocks(a["sk"], a["sv"], a["dk"], a["dv"], a["p"], a["n"], a["snb"],
-                                  a["dnb"], a["bs"], a["hkv"], a["d"], None)
+        return no_launch(lib.pa_swap_blocks(a["sk"], a["sv"], a["dk"], a["dv"], a["p"], a["n"], a["snb"],
+                                  a["dnb"], a["bs"], a["hkv"], a["d"], None))
 
     assert call(n=0) == 0
     assert call(n=-1) == -2

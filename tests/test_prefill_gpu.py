@@ -1,6 +1,7 @@
 """pa_prefill on the GPU against the float64 oracle: the 8 x 2048 causal
 workload, ragged varlen batches with every grouped-head ratio, prompts with a
-cached prefix (bottom-right causal alignment), stress inputs, and
+cached prefix (bottom-right causal alignment), long prefixes whose query
+blocks are split across workgroups and merged, stress inputs, and
 consistency with pa_decode (row i of a prompt = decode at length i+1)."""
 
 import numpy as np
@@ -21,8 +22,10 @@ def run_prefill(dev):
     pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
     out = torch.full((case.total_q_rows, case.num_q_heads, case.head_dim), float("nan"),
                      dtype=torch.bfloat16, device="cuda")
+    ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len, case.num_q_heads,
+                                    case.num_kv_heads, case.max_blocks_per_seq)
     pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache, dev.v_cache,
-               dev.block_table, case.scale)
+               dev.block_table, case.scale, ws)
     torch.cuda.synchronize()
     return out
 
@@ -79,6 +82,49 @@ def test_multi_query_decode():
     """Speculative verification: 4 new tokens per sequence, causal among
     themselves, over U{512..4096} cached tokens."""
     check(wl.multi_query_decode())
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8)])
+def test_prefill_long_prefix_split_many_ways(hq, hkv):
+    """Query blocks over cached prefixes of up to 20,000 keys: their key
+    ranges are cut into up to 10 parts, one workgroup each, merged through
+    the workspace by the last part to finish."""
+    ctx = [20000, 9000, 300, 12345]
+    qlens = [100, 64, 30, 1]
+    case = wl.make_case(f"longprefix_{hq}_{hkv}", "prefill", 45 + hq, ctx, hq, hkv, q_lens=qlens)
+    assert pa.prefill_workspace_size(case.batch, case.total_q_rows, case.max_q_len, hq, hkv,
+                                     case.max_blocks_per_seq) > 0
+    check(case, seqs_full={1, 2, 3}, heads_sampled=[0, hq - 1])
+
+
+def test_long_prefix_chunk():
+    """A 512-token chunk over a 65,536-token cached prefix: 64 query blocks
+    for 256 CUs, so each block's context is split across workgroups."""
+    case = wl.long_prefix_chunk()
+    assert pa.prefill_workspace_size(case.batch, case.total_q_rows, case.max_q_len, 16, 8,
+                                     case.max_blocks_per_seq) > 0
+    check(case, seqs_full=set(), heads_sampled=[0, 5, 15])
+
+
+def test_prefill_split_repeat_is_bit_identical():
+    """Two calls on one workspace give the same bits: the merge order is
+    fixed and nothing depends on what the workspace held before."""
+    case = wl.make_case("repeat", "prefill", 46, [9000, 5000, 40], 16, 8, q_lens=[300, 130, 40])
+    dev = place(case)
+    pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+    ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len, 16, 8,
+                                    case.max_blocks_per_seq)
+    outs = []
+    for k in range(3):
+        ws.fill_(0xFF if k == 1 else 0x00)  # NaN patterns in the scratch must not matter
+        out = torch.full((case.total_q_rows, 16, 128), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache,
+                   dev.v_cache, dev.block_table, case.scale, ws)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert not torch.isnan(outs[0].view(torch.bfloat16)).any()
 
 
 def test_prefill_stress_peaked_softmax():

@@ -106,6 +106,11 @@ def test_configs_shapes_and_rules():
     assert c7.batch == 64 and np.all(c7.q_lens == 4) and c7.total_q_rows == 256
     _check_tables(c7)
 
+    c8 = wl.long_prefix_chunk()
+    assert c8.batch == 1 and c8.total_q_rows == 512 and int(c8.context_lens[0]) == 65536 + 512
+    assert c8.max_blocks_per_seq == (65536 + 512) // 256
+    _check_tables(c8)
+
 
 def test_step_and_history_rows_partition_the_cache():
     c = wl.make_case("x", "decode", 5, [1, 4, 300], 4, 2)

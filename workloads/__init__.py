@@ -348,6 +348,12 @@ def multi_query_decode() -> PagedCase:
                      q_lens=np.full(64, 4, dtype=np.int64), rng=rng)
 
 
+def long_prefix_chunk() -> PagedCase:
+    """One long prompt mid-way through chunked prefill: a 512-token chunk on
+    top of a 65,536-token cached prefix, one sequence; 16 q / 8 kv heads."""
+    return make_case("long_prefix_chunk", "prefill", 8, [65536 + 512], 16, 8, q_lens=[512])
+
+
 CONFIGS = {
     "tiny_decode": tiny_decode,
     "qwen3_0.6b_decode": qwen3_0_6b_decode,
@@ -356,6 +362,7 @@ CONFIGS = {
     "long_context_decode": long_context_decode,
     "chunked_prefill_mixed": chunked_prefill_mixed,
     "multi_query_decode": multi_query_decode,
+    "long_prefix_chunk": long_prefix_chunk,
 }
 
 
