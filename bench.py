@@ -221,6 +221,42 @@ def varlen_report(name: str, steps: int, warmup: int) -> dict:
             "store_ms": round(sto, 4)}
 
 
+def decode_multi_report(steps: int, warmup: int) -> dict:
+    """pa_decode_multi on the multi-query decode workload (4 new tokens per
+    sequence scored in one pass): the K/V bytes of every context read once,
+    over the HBM peak."""
+    c = wl.multi_query_decode()
+    ql = int(c.q_lens[0])
+    dev = place(c)
+    pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+    out = torch.empty((c.total_q_rows, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = pa.alloc_decode_multi_workspace(c.batch, ql, c.num_q_heads, c.num_kv_heads)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa.decode_multi(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens, ql,
+                        c.max_context_len, c.scale, ws)
+
+    for _ in range(warmup):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kvb = int(c.context_lens.sum()) * c.num_kv_heads * c.head_dim * 2 * 2
+    gbs = kvb / (ms * 1e-3) / 1e9
+    del dev, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": c.name, "entry_point": "pa_decode_multi", "q_per_seq": ql,
+            "decode_ms": round(ms, 4), "kv_GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def blocks_report(steps: int, warmup: int) -> dict:
     """pa_copy_blocks over 512 block pairs of a 2,048-block pool (8 kv heads:
     1 MiB of K+V per block, so 512 MiB read + 512 MiB written per call), and
@@ -562,6 +598,8 @@ def main(argv=None):
         for name in ("chunked_prefill_mixed", "multi_query_decode", "long_prefix_chunk"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(10, args.steps // 5), 3)
+        print("[bench] extra multi-query decode (pa_decode_multi)", file=sys.stderr, flush=True)
+        extra["multi_query_decode_multi"] = decode_multi_report(max(10, args.steps // 5), 3)
         print("[bench] extra block copy / swap", file=sys.stderr, flush=True)
         extra["blocks"] = blocks_report(max(10, args.steps // 5), 3)
         print("[bench] extra block manager (host)", file=sys.stderr, flush=True)

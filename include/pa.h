@@ -160,6 +160,41 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * pa_decode_multi -- decode of q_per_seq new tokens per sequence at once
+ * (speculative verification: the drafted tokens and the next one scored in
+ * one pass), each attending causally to the cache.
+ *
+ * Query row i (0 <= i < q_per_seq) of sequence b is the token at position
+ * context_lens[b] - q_per_seq + i and attends to the cached positions
+ * 0 .. context_lens[b] - q_per_seq + i of its sequence (the same bottom-right
+ * causal rule as pa_prefill; the K/V of all context_lens[b] positions,
+ * including the new tokens, must already be in the cache).  Softmax and
+ * rounding as in pa_decode; q_per_seq = 1 is exactly pa_decode.
+ *
+ *   out, q        : bf16 [batch * q_per_seq][num_q_heads][head_dim], row
+ *                   b * q_per_seq + i, 16-B aligned.
+ *   q_per_seq     : 1 .. 8, with q_per_seq * num_q_heads / num_kv_heads <= 8
+ *                   (else PA_ERR_UNSUPPORTED): the rows of one (sequence, kv
+ *                   head) are processed together like the query heads of one
+ *                   kv head in pa_decode.
+ *   context_lens  : int32 [batch], each >= q_per_seq for meaningful rows (a
+ *                   row whose position is negative sees no key and is zero).
+ *   workspace     : >= pa_decode_multi_workspace_size(...) bytes; same rules
+ *                   as pa_decode's workspace.
+ *   Other arguments as for pa_decode.
+ *   Source: CSDN essay, first and third sections (the decode kernel); the
+ *   causal rule of the prefill description on the same pages.
+ */
+size_t pa_decode_multi_workspace_size(int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size);
+int pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t batch, int32_t q_per_seq,
+                    int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_workspace_size -- bytes of device workspace pa_prefill needs for
  * these sizes (0 when no query block can be split: contexts of at most
  * 2048 tokens, i.e. max_blocks_per_seq <= 8).  Also 0 for invalid arguments;

@@ -33,7 +33,8 @@ STATUS_NAMES = {
     -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT", -10: "PA_ERR_NO_BLOCKS",
 }
 
-EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_prefill_workspace_size",
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_multi_workspace_size",
+           "pa_decode_multi", "pa_prefill_workspace_size",
            "pa_prefill",
            "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append",
@@ -73,6 +74,11 @@ def lib() -> ctypes.CDLL:
         l.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_decode.restype = ctypes.c_int
+        l.pa_decode_multi_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+        l.pa_decode_multi_workspace_size.restype = _sz
+        l.pa_decode_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]
+        l.pa_decode_multi.restype = ctypes.c_int
         l.pa_prefill_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
         l.pa_prefill_workspace_size.restype = _sz
         l.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _i32,
@@ -209,6 +215,43 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_len:
         _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(k_cache, "k_cache", _BF16),
         _dev(v_cache, "v_cache", _BF16), _dev(block_table, "block_table", _I32),
         int(block_table.shape[1]), _dev(context_lens, "context_lens", _I32), b,
+        int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        _dev(workspace, "workspace", (torch.uint8, torch.float32, torch.int32)),
+        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+
+
+def decode_multi_workspace_size(batch: int, q_per_seq: int, num_q_heads: int,
+                                num_kv_heads: int) -> int:
+    n = lib().pa_decode_multi_workspace_size(batch, q_per_seq, num_q_heads, num_kv_heads, HEAD_DIM,
+                                             BLOCK_SIZE)
+    if n == 0 and batch > 0:
+        raise PAError(-3, "no workspace size for these shapes (q_per_seq * Hq/Hkv must be <= 8)")
+    return int(n)
+
+
+def alloc_decode_multi_workspace(batch: int, q_per_seq: int, num_q_heads: int, num_kv_heads: int,
+                                 device="cuda"):
+    """A zero-filled pa_decode_multi workspace (its counters are reset by
+    every call, so it can be reused)."""
+    n = decode_multi_workspace_size(batch, q_per_seq, num_q_heads, num_kv_heads)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode_multi(out, q, k_cache, v_cache, block_table, context_lens, q_per_seq: int,
+                 max_context_len: int, scale: float, workspace, stream=None) -> None:
+    """pa_decode_multi: q/out [B * q_per_seq, Hq, 128] (row b*q_per_seq + i),
+    block_table int32 [B, max_blocks_per_seq], context_lens int32 [B]."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    rows, hq, d = (int(x) for x in q.shape)
+    b = int(context_lens.shape[0])
+    if tuple(out.shape) != (rows, hq, d) or rows != b * int(q_per_seq):
+        raise ValueError("q and out must be [B * q_per_seq, Hq, head_dim]")
+    if block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    _check(lib().pa_decode_multi(
+        _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(k_cache, "k_cache", _BF16),
+        _dev(v_cache, "v_cache", _BF16), _dev(block_table, "block_table", _I32),
+        int(block_table.shape[1]), _dev(context_lens, "context_lens", _I32), b, int(q_per_seq),
         int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         _dev(workspace, "workspace", (torch.uint8, torch.float32, torch.int32)),
         workspace.numel() * workspace.element_size(), _stream(q, stream)))

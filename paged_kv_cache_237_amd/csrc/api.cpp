@@ -143,6 +143,85 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
   return ps;
 }
 
+// Virtual heads per (sequence, kv head) of a decode of q_per_seq rows: group
+// * q_per_seq rounded up to a power of two; 0 if that exceeds 8.
+int virtual_group(int group, int32_t q_per_seq) {
+  if (q_per_seq < 1 || q_per_seq > 8) return 0;
+  int gv = 1;
+  while (gv < group * q_per_seq) gv *= 2;
+  return gv <= 8 ? gv : 0;
+}
+
+// Decode of q_per_seq query rows per sequence (1 for pa_decode).
+int decode_rows(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t batch, int32_t q_per_seq, int32_t max_context_len, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
+    int group = 0;
+    int r = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group);
+    if (r != PA_OK) return r;
+    if (q_per_seq < 1) return fail(PA_ERR_BAD_SHAPE, "q_per_seq must be >= 1");
+    const int gv = virtual_group(group, q_per_seq);
+    if (gv == 0)
+      return fail(PA_ERR_UNSUPPORTED, "q_per_seq * num_q_heads / num_kv_heads must be at most 8");
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq must be positive");
+    if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
+    if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE)
+      return fail(PA_ERR_BAD_SHAPE, "max_context_len outside [0, max_blocks_per_seq*block_size]");
+    if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
+    if (batch == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens)
+      return fail(PA_ERR_NULL_PTR, "pa_decode: a pointer argument is NULL");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(context_lens, 4))
+      return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, int32 arrays 4-byte");
+    // every tile index of the flattened work list must fit an int
+    if (int64_t(batch) * num_kv_heads * max_blocks_per_seq * (PA_BLOCK_SIZE / pa::kTile) >
+        int64_t(INT32_MAX) / 2)
+      return fail(PA_ERR_BAD_SHAPE, "batch * num_kv_heads * max_blocks_per_seq too large");
+    int cus = 0;
+    r = current_cus(&cus);
+    if (r != PA_OK) return r;
+    const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len, gv);
+    const size_t need = decode_ws_bytes(batch, num_kv_heads, gv, waves);
+    if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                        std::to_string(workspace_bytes));
+    pa::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint4*>(k_cache);
+    a.v_cache = static_cast<const uint4*>(v_cache);
+    a.block_table = block_table;
+    a.ctx_lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    a.counters = static_cast<int*>(workspace);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    decode_counter_bytes(batch, num_kv_heads));
+    a.num_blocks = num_blocks;
+    a.batch = batch;
+    a.hkv = num_kv_heads;
+    a.mbps = max_blocks_per_seq;
+    a.n_waves = int(waves);
+    a.run_w_even = pa::kRunWeightEven;
+    a.run_w_odd = pa::kRunWeightOdd;
+    a.scale_log2 = float(double(scale) * 1.4426950408889634);
+    a.ql = q_per_seq;
+    a.gr = group;
+    a.gr_shift = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
+    a.hq = num_q_heads;
+    const hipError_t e = pa::launch_decode(a, gv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected host exception");
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,14 +418,21 @@ int pa_store_kv(const void* k_new, const void* v_new, const int32_t* slot_mappin
 
 size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size) {
+  return pa_decode_multi_workspace_size(batch, 1, num_q_heads, num_kv_heads, head_dim, block_size);
+}
+
+size_t pa_decode_multi_workspace_size(int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
   try {
     int group = 0;
     if (batch < 0) return 0;
     if (check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group) != PA_OK) return 0;
+    const int gv = virtual_group(group, q_per_seq);
+    if (gv == 0) return 0;
     int cus = 0;
     if (current_cus(&cus) != PA_OK) return 0;
     const int64_t waves = int64_t(cus) * pa::kDecodeWavesPerCU;
-    return decode_ws_bytes(batch, num_kv_heads, group, waves);
+    return decode_ws_bytes(batch, num_kv_heads, gv, waves);
   } catch (...) {
     return 0;
   }
@@ -358,60 +444,20 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
               void* stream) {
-  try {
-    if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
-    int group = 0;
-    int r = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group);
-    if (r != PA_OK) return r;
-    if (max_blocks_per_seq <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq must be positive");
-    if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
-    if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE)
-      return fail(PA_ERR_BAD_SHAPE, "max_context_len outside [0, max_blocks_per_seq*block_size]");
-    if (!std::isfinite(scale)) return fail(PA_ERR_BAD_SHAPE, "scale is not finite");
-    if (batch == 0) return ok();
-    if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens)
-      return fail(PA_ERR_NULL_PTR, "pa_decode: a pointer argument is NULL");
-    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(block_table, 4) || !aligned(context_lens, 4))
-      return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, int32 arrays 4-byte");
-    // every tile index of the flattened work list must fit an int
-    if (int64_t(batch) * num_kv_heads * max_blocks_per_seq * (PA_BLOCK_SIZE / pa::kTile) >
-        int64_t(INT32_MAX) / 2)
-      return fail(PA_ERR_BAD_SHAPE, "batch * num_kv_heads * max_blocks_per_seq too large");
-    int cus = 0;
-    r = current_cus(&cus);
-    if (r != PA_OK) return r;
-    const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len, group);
-    const size_t need = decode_ws_bytes(batch, num_kv_heads, group, waves);
-    if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
-    if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
-                                        std::to_string(workspace_bytes));
-    pa::DecodeArgs a;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint4*>(k_cache);
-    a.v_cache = static_cast<const uint4*>(v_cache);
-    a.block_table = block_table;
-    a.ctx_lens = context_lens;
-    a.out = static_cast<uint16_t*>(out);
-    a.counters = static_cast<int*>(workspace);
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    decode_counter_bytes(batch, num_kv_heads));
-    a.num_blocks = num_blocks;
-    a.batch = batch;
-    a.hkv = num_kv_heads;
-    a.mbps = max_blocks_per_seq;
-    a.n_waves = int(waves);
-    a.run_w_even = pa::kRunWeightEven;
-    a.run_w_odd = pa::kRunWeightOdd;
-    a.scale_log2 = float(double(scale) * 1.4426950408889634);
-    const hipError_t e = pa::launch_decode(a, group, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    return ok();
-  } catch (...) {
-    return fail(PA_ERR_HIP, "unexpected host exception");
-  }
+  return decode_rows(out, q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens, batch, 1,
+                     max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     workspace, workspace_bytes, stream);
+}
+
+int pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t batch, int32_t q_per_seq,
+                    int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_rows(out, q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens, batch,
+                     q_per_seq, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, scale, workspace, workspace_bytes, stream);
 }
 
 size_t pa_prefill_workspace_size(int32_t batch, int64_t total_q_rows, int32_t max_seqlen_q,

@@ -76,6 +76,19 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
   return ((cint*)p)[i];
 }
 
+// Query/output row of virtual head v of segment (b, g), and whether it is a
+// real query row (not padding).  Without the causal rows (one query row per
+// sequence) the G heads of a kv head are simply contiguous.
+template <int G, bool Causal>
+__device__ __forceinline__ int64_t vrow(const DecodeArgs& a, int b, int g, int v) {
+  if constexpr (!Causal) return (int64_t(b) * a.hkv + g) * G + v;
+  return (int64_t(b) * a.ql + (v >> a.gr_shift)) * a.hq + int64_t(g) * a.gr + (v & (a.gr - 1));
+}
+template <bool Causal>
+__device__ __forceinline__ bool vreal(const DecodeArgs& a, int v) {
+  return !Causal || (v >> a.gr_shift) < a.ql;
+}
+
 // Number of tiles of all segments (identical in every lane).
 __device__ int total_tiles(const DecodeArgs& a) {
   const int lane = lane_id();
@@ -182,10 +195,9 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
 // Merge the partial records of segment `seg` written by waves w0..w1 into
 // its G output rows (lane = 2 dims).  One pass with an online rescale; the
 // loads of four records are issued together.
-template <int G>
+template <int G, bool Causal>
 __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0, int w1) {
   const int lane = lane_id();
-  const int hq = a.hkv * G;
   float M[G], L[G], U0[G], U1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -220,11 +232,12 @@ __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0
         M[h] = mn;
       }
   }
-  uint32_t* out = reinterpret_cast<uint32_t*>(a.out + (int64_t(b) * hq + g * G) * kDim);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    if (!vreal<Causal>(a, h)) continue;
     const float inv = L[h] > 0.f ? 1.f / L[h] : 0.f;
-    out[h * (kDim / 2) + lane] = pack_bf16x2(U0[h] * inv, U1[h] * inv);
+    uint32_t* out = reinterpret_cast<uint32_t*>(a.out + vrow<G, Causal>(a, b, g, h) * kDim);
+    out[lane] = pack_bf16x2(U0[h] * inv, U1[h] * inv);
   }
 }
 
@@ -273,14 +286,13 @@ __device__ __forceinline__ void issue_v(const TileLoads& tl, uint4 (&vr)[16]) {
 // fold of the row partials and either the bf16 output (whole segment) or a
 // partial record at seg + wave.  Returns the number of cut segments, whose
 // (b, g, first run, last run) are stored in pend_*.
-template <int G>
+template <int G, bool Causal>
 __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& runs, int wave, uint4* q_lds,
                           float* p_lds, int* prog, int wv, int (&pend_b)[2], int (&pend_g)[2],
                           int (&pend_w0)[2], int (&pend_w1)[2]) {
   constexpr int NW = GroupShape<G>::kWaves;
   int done = 0;  // tiles streamed by this wave
   const int lane = lane_id();
-  const int hq = a.hkv * G;
   constexpr int kQPerLane = (G * kChunks + kWave - 1) / kWave;
 
   int b, before;
@@ -298,9 +310,16 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
   ctx = __builtin_amdgcn_readfirstlane(ctx);
 
   // prologue: q of the first segment, loads of the first tile
-  {
-    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * hq + g * G) * kDim);
+  if constexpr (!Causal) {
+    // one query row per sequence: the G heads are contiguous
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + vrow<G, Causal>(a, b, g, 0) * kDim);
     for (int i = lane; i < G * kChunks; i += kWave) q_lds[i] = qsrc[i];
+  } else {
+    for (int i = lane; i < G * kChunks; i += kWave) {
+      const int v = i / kChunks;
+      q_lds[i] = vreal<Causal>(a, v) ? reinterpret_cast<const uint4*>(a.q + vrow<G, Causal>(a, b, g, v) * kDim)[i % kChunks]
+                             : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   TileLoads cur = tile_loads(a, ld_uniform(a.block_table, int64_t(b) * a.mbps + (t >> 2)), g, t, ctx);
   uint4 kr[kChunks], vr[16];
@@ -316,7 +335,7 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  const int vrow = lane >> 4;  // row within a 4-row V load
+  const int vrow4 = lane >> 4;  // row within a 4-row V load
   int piece_t0 = t;            // first tile of the current piece
   int npend = 0;
 
@@ -340,11 +359,22 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
     const bool next_ok = has_next && nb < a.batch;
     uint4 qn[kQPerLane];
     if (seg_end && next_ok) {
-      const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(nb) * hq + ng * G) * kDim);
+      if constexpr (!Causal) {
+        const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + vrow<G, Causal>(a, nb, ng, 0) * kDim);
 #pragma unroll
-      for (int j = 0; j < kQPerLane; ++j) {
-        const int i = lane + j * kWave;
-        qn[j] = i < G * kChunks ? qsrc[i] : make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < kQPerLane; ++j) {
+          const int i = lane + j * kWave;
+          qn[j] = i < G * kChunks ? qsrc[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kQPerLane; ++j) {
+          const int i = lane + j * kWave;
+          const int v = i / kChunks;
+          qn[j] = i < G * kChunks && vreal<Causal>(a, v)
+                      ? reinterpret_cast<const uint4*>(a.q + vrow<G, Causal>(a, nb, ng, v) * kDim)[i % kChunks]
+                      : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
     // past the end of the run the "next tile" has no block: its loads are
@@ -393,11 +423,16 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
     __builtin_amdgcn_sched_barrier(0);
 
     // --- online softmax (log2 domain)
+    const int key = t * kTile + lane;
+    const int last0 = ctx - a.ql;  // last key of query row 0 of the sequence
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       // additive mask: keeps the dot products unconditional (a select on
-      // kval would let the compiler sink them into a branch)
-      const float sh = fmaf(s[h], a.scale_log2, kval ? 0.f : -INFINITY);
+      // kval would let the compiler sink them into a branch); with several
+      // query rows per sequence, row h >> gr_shift sees keys up to
+      // last0 + that row
+      const bool vis = Causal ? kval && key <= last0 + (h >> a.gr_shift) : kval;
+      const float sh = fmaf(s[h], a.scale_log2, vis ? 0.f : -INFINITY);
       const float mn = fmaxf(m[h], wave_max(sh));
       const float ref = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m[h] - ref);
@@ -413,7 +448,7 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
     // --- PV of the current tile
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float* pp = p_lds + (4 * k + vrow) * G;
+      const float* pp = p_lds + (4 * k + vrow4) * G;
       float pv[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) pv[h] = pp[h];
@@ -450,11 +485,12 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
         if (lane < 16) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
+            if (!vreal<Causal>(a, h)) continue;
             const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = acc[h][e] * inv;
-            uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t(b) * hq + g * G + h) * kDim);
+            uint4* dst = reinterpret_cast<uint4*>(a.out + vrow<G, Causal>(a, b, g, h) * kDim);
             dst[lane] = pack8(o);
           }
         }
@@ -511,7 +547,7 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
   return npend;
 }
 
-template <int G>
+template <int G, bool Causal>
 __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = GroupShape<G>::kWaves;
   __shared__ uint4 q_lds[NW][G * kChunks];
@@ -524,11 +560,10 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
 
   // Empty contexts have no tiles: their output rows are zero.
   if (wave < a.n_waves) {
-    const int hq = a.hkv * G;
     for (int bb = wave; bb < a.batch; bb += a.n_waves) {
       if (clamp_ctx(a, a.ctx_lens[bb]) != 0) continue;
-      uint32_t* o = reinterpret_cast<uint32_t*>(a.out + int64_t(bb) * hq * kDim);
-      for (int i = lane_id(); i < hq * (kDim / 2); i += kWave) o[i] = 0u;
+      uint32_t* o = reinterpret_cast<uint32_t*>(a.out + int64_t(bb) * a.ql * a.hq * kDim);
+      for (int i = lane_id(); i < a.ql * a.hq * (kDim / 2); i += kWave) o[i] = 0u;
     }
   }
 
@@ -545,7 +580,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   // are counted once the whole run has been streamed, so the record stores
   // never stall the loads.
   int pend_b[2], pend_g[2], pend_w0[2], pend_w1[2];
-  const int npend = stream_run<G>(a, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
+  const int npend = stream_run<G, Causal>(a, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
                                   pend_g, pend_w0, pend_w1);
   // a finished wave no longer holds its siblings back
   if (lane_id() == 0) prog[wv] = 1 << 30;
@@ -562,7 +597,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
         prev = __hip_atomic_fetch_add(a.counters + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = __builtin_amdgcn_readfirstlane(prev);
       if (prev == pend_w1[i] - pend_w0[i]) {
-        merge_segment<G>(a, seg, pend_b[i], pend_g[i], pend_w0[i], pend_w1[i]);
+        merge_segment<G, Causal>(a, seg, pend_b[i], pend_g[i], pend_w0[i], pend_w1[i]);
         if (lane_id() == 0)
           __hip_atomic_store(a.counters + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -574,7 +609,11 @@ template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
   constexpr int NW = GroupShape<G>::kWaves;
   const unsigned split_blocks = unsigned((a.n_waves + NW - 1) / NW);
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0, s, a);
+  // one query row per sequence needs no causal mask inside the context
+  if (a.ql == 1)
+    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -48,6 +48,15 @@ struct DecodeArgs {
   int run_w_even;  // relative run length of waves on even- / odd-numbered XCDs
   int run_w_odd;
   float scale_log2;  // scale * log2(e)
+  // Query rows: ql per sequence (1 for decode), gr q heads per kv head, hq q
+  // heads.  The kernel's G = gr * ql rounded up to a power of two "virtual
+  // heads" per (sequence, kv head): virtual head v is query token
+  // b*ql + (v >> gr_shift), head g*gr + (v & (gr-1)); it sees keys
+  // 0 .. ctx - ql + (v >> gr_shift).  Virtual heads past ql rows are padding.
+  int ql;
+  int gr;
+  int gr_shift;
+  int hq;
 };
 
 struct PrefillArgs {

@@ -111,6 +111,32 @@ def test_decode_rejects_bad_arguments_on_the_host():
 
 
 @needs_lib
+def test_decode_multi_rejects_bad_arguments_on_the_host():
+    lib = pa.lib()
+    base = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=4, cl=FAKE, b=2, ql=4, maxc=300,
+                hq=16, hkv=8, d=128, bs=256, nb=8, scale=0.088, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return no_launch(lib.pa_decode_multi(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"],
+                                             a["cl"], a["b"], a["ql"], a["maxc"], a["hq"], a["hkv"],
+                                             a["d"], a["bs"], a["nb"], a["scale"], a["ws"], a["wsb"],
+                                             None))
+
+    assert call(b=0) == 0
+    assert call(ql=0) == -2
+    assert call(ql=5) == -3           # 2 heads x 5 rows: 16 virtual heads
+    assert call(ql=9) == -3
+    assert call(hq=64, ql=2) == -3    # G = 8 leaves room for one row only
+    assert call(hq=24) == -3          # G = 3
+    assert call(maxc=-1) == -2
+    assert call(q=None) == -1
+    assert call(out=FAKE + 8) == -4
+    assert lib.pa_decode_multi_workspace_size(2, 0, 16, 8, 128, 256) == 0
+    assert lib.pa_decode_multi_workspace_size(2, 5, 16, 8, 128, 256) == 0
+
+
+@needs_lib
 def test_prefill_rejects_bad_arguments_on_the_host():
     """Every call below either fails a host check or returns before the
     launch (an empty batch or no query rows): the pointers are fake, so a
