@@ -346,13 +346,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[ms][r] = 0.f;
+    // K operands are read 8 ahead of the MFMAs that use them
+    uint4 ka[8][2];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) ka[ks][ms] = ksrc[2 * ks * kKeys + 32 * ms];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms) {
-        const bf16x8_t ka = as_bf16x8(ksrc[2 * ks * kKeys + 32 * ms]);
-        s[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], s[ms], 0, 0, 0);
+        ka[ks + 4][ms] = ksrc[2 * (ks + 4) * kKeys + 32 * ms];
+        s[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[ks][ms]), qop[ks], s[ms], 0, 0, 0);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 4; ks < 8; ++ks) {
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms)
+        s[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[ks][ms]), qop[ks], s[ms], 0, 0, 0);
     }
   };
 
