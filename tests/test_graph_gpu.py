@@ -1,8 +1,10 @@
-"""The decode step (pa_store_kv then pa_decode) captured in a HIP graph and
-replayed: every replay must give the same bits as the eager calls, also with
-other eager work and synchronisations between replays.  The library's
-kernels use no memset nodes; the decode workspace counters are reset by the
-kernel itself, so replays need no re-initialisation."""
+"""Steps captured in a HIP graph and replayed: the decode step (pa_store_kv
+then pa_decode), a prefill whose query blocks are split across workgroups
+(attention and merge kernels), and pa_decode_multi.  Every replay must give
+the same bits as the eager calls, also with other eager work and
+synchronisations between replays.  The library's kernels use no memset
+nodes; the decode workspace counters are reset by the kernel itself and the
+prefill workspace is scratch, so replays need no re-initialisation."""
 
 import numpy as np
 import pytest
@@ -56,3 +58,60 @@ def test_graph_replays_match_eager(name):
     ref = oracle.decode(wl.bits_to_numpy(case.q_all()), kp, vp, case.block_table,
                         case.context_lens, case.scale)
     compare(bf16_out_to_f64(out), ref, f"{name} graph")
+
+
+def replay_and_check(step, out, what):
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        scratch = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"{what} replay {i}"
+        del scratch
+
+
+def test_graph_prefill_with_split_blocks():
+    case = wl.long_prefix_chunk()
+    print(f"[graph] {case.name}", flush=True)
+    dev = place(case)
+    out = torch.zeros((case.total_q_rows, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len,
+                                    case.num_q_heads, case.num_kv_heads, case.max_blocks_per_seq)
+    assert ws is not None  # the launch splits its query blocks
+
+    def step():
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache,
+                   dev.v_cache, dev.block_table, case.scale, ws)
+
+    replay_and_check(step, out, case.name)
+
+
+def test_graph_decode_multi():
+    case = wl.multi_query_decode()
+    print(f"[graph] {case.name} pa_decode_multi", flush=True)
+    dev = place(case)
+    ql = int(case.q_lens[0])
+    out = torch.zeros((case.total_q_rows, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    ws = pa.alloc_decode_multi_workspace(case.batch, ql, case.num_q_heads, case.num_kv_heads)
+
+    def step():
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        pa.decode_multi(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens, ql,
+                        case.max_context_len, case.scale, ws)
+
+    replay_and_check(step, out, case.name)
