@@ -92,7 +92,8 @@ enum pa_status {
   PA_ERR_SLOT_RANGE = -7,    /* pa_validate_slots: a slot >= num_slots */
   PA_ERR_DUPLICATE_SLOT = -8, /* pa_validate_slots: two tokens share a slot */
   PA_ERR_BLOCK_CONFLICT = -9, /* pa_validate_block_pairs: a block written twice, or read and written */
-  PA_ERR_NO_BLOCKS = -10      /* block manager: not enough free blocks */
+  PA_ERR_NO_BLOCKS = -10,     /* block manager: not enough free blocks */
+  PA_ERR_PRECONDITION = -11   /* debug checks: a data-dependent precondition is violated */
 };
 
 /*
@@ -362,6 +363,23 @@ int pa_bm_block_table(pa_block_manager* bm, const int64_t* seqs, int32_t n, int3
 /* Cache slots of positions first_pos .. first_pos+count-1 of `seq`. */
 int pa_bm_slot_mapping(pa_block_manager* bm, int64_t seq, int64_t first_pos, int64_t count,
                        int32_t* slots_out);
+
+/*
+ * Debug checks of the data-dependent preconditions on the device.  When on
+ * (environment variable PA_DEBUG=1 at the first call, or this call), every
+ * pa_store_kv, pa_decode, pa_decode_multi and pa_prefill first runs a small
+ * kernel on its stream that checks the device-resident inputs -- slots
+ * inside the pool; context_lens inside [0, min(max_context_len,
+ * max_blocks_per_seq * block_size)]; every block-table entry a sequence uses
+ * inside [0, num_blocks); for pa_prefill cu_seqlens_q[0] = 0, 0 <= q_len_b
+ * <= min(context_lens[b], max_seqlen_q) and cu_seqlens_q[batch] =
+ * total_q_rows; for pa_decode_multi context_lens[b] >= q_per_seq -- then
+ * SYNCHRONISES the stream and returns PA_ERR_PRECONDITION (detail naming the
+ * violated conditions) without launching the call's own kernels.  Duplicate
+ * slots are left to pa_validate_slots.  Not for use under graph capture.
+ * Returns the previous setting (1 on, 0 off).
+ */
+int pa_set_debug_checks(int enabled);
 
 /* Name of a status code ("PA_OK", "PA_ERR_NULL_PTR", ...); never NULL. */
 const char* pa_status_string(int status);

@@ -30,7 +30,7 @@ PA_OK = 0
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL_PTR", -2: "PA_ERR_BAD_SHAPE", -3: "PA_ERR_UNSUPPORTED",
     -4: "PA_ERR_ALIGN", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP", -7: "PA_ERR_SLOT_RANGE",
-    -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT", -10: "PA_ERR_NO_BLOCKS",
+    -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT", -10: "PA_ERR_NO_BLOCKS", -11: "PA_ERR_PRECONDITION",
 }
 
 EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_multi_workspace_size",
@@ -39,7 +39,7 @@ EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_mu
            "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append",
            "pa_bm_append_batch", "pa_bm_fork", "pa_bm_free", "pa_bm_seq_len", "pa_bm_block_table", "pa_bm_slot_mapping",
-           "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
+           "pa_set_debug_checks", "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
 
 
 class PAError(RuntimeError):
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         l.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _i32,
                                  _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_prefill.restype = ctypes.c_int
+        l.pa_set_debug_checks.argtypes = [ctypes.c_int]
+        l.pa_set_debug_checks.restype = ctypes.c_int
         l.pa_status_string.argtypes = [ctypes.c_int]
         l.pa_status_string.restype = ctypes.c_char_p
         l.pa_last_error_detail.argtypes = []
@@ -294,6 +296,12 @@ def prefill(out, q, cu_seqlens_q, context_lens, max_seqlen_q: int, k_cache, v_ca
         _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
         _dev(block_table, "block_table", _I32), int(block_table.shape[1]), hq, hkv, d,
         BLOCK_SIZE, nb, float(scale), ws_ptr, ws_bytes, _stream(q, stream)))
+
+
+def set_debug_checks(enabled: bool) -> bool:
+    """Turn the library's device-side precondition checks on or off (calls
+    then synchronise their stream); returns the previous setting."""
+    return bool(lib().pa_set_debug_checks(1 if enabled else 0))
 
 
 def validate_slots(slots_host, num_slots: int) -> int:

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "prefill.hip", "blocks.hip",
-           "block_manager.cpp"]
+           "block_manager.cpp", "checks.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5",

@@ -10,6 +10,8 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <atomic>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -68,6 +70,30 @@ int current_cus(int* cus) {
 }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Debug checks: -1 = not yet decided (PA_DEBUG is read at the first call).
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks_on() {
+  int v = g_debug_checks.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("PA_DEBUG");
+    v = (e != nullptr && e[0] == '1') ? 1 : 0;
+    int expected = -1;
+    if (!g_debug_checks.compare_exchange_strong(expected, v)) v = expected;
+  }
+  return v == 1;
+}
+
+// PA_ERR_PRECONDITION naming the conditions whose bits are set.
+int precondition_fail(int flags) {
+  std::string d = "device checks:";
+  if (flags & pa::kCheckSlot) d += " a slot past the pool;";
+  if (flags & pa::kCheckCtx) d += " a context length outside [0, cap];";
+  if (flags & pa::kCheckTable) d += " a used block-table entry outside the pool;";
+  if (flags & pa::kCheckRows) d += " query rows inconsistent with cu_seqlens_q or the context;";
+  return fail(PA_ERR_PRECONDITION, d);
+}
 
 int check_geometry(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                    int32_t block_size, int* group) {
@@ -214,6 +240,21 @@ int decode_rows(void* out, const void* q, const void* k_cache, const void* v_cac
     a.gr = group;
     a.gr_shift = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
     a.hq = num_q_heads;
+    if (debug_checks_on()) {
+      pa::SeqCheckArgs c{};
+      c.ctx_lens = context_lens;
+      c.block_table = block_table;
+      c.cu_q = nullptr;
+      c.num_blocks = num_blocks;
+      c.batch = batch;
+      c.mbps = max_blocks_per_seq;
+      c.max_context_len = max_context_len;
+      c.rows_per_seq = q_per_seq;
+      int flags = 0;
+      const hipError_t ce = pa::check_seqs(c, static_cast<hipStream_t>(stream), &flags);
+      if (ce != hipSuccess) return hip_fail(ce, "decode checks");
+      if (flags) return precondition_fail(flags);
+    }
     const hipError_t e = pa::launch_decode(a, gv, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
@@ -225,6 +266,12 @@ int decode_rows(void* out, const void* q, const void* k_cache, const void* v_cac
 }  // namespace
 
 extern "C" {
+
+int pa_set_debug_checks(int enabled) {
+  const int prev = debug_checks_on() ? 1 : 0;
+  g_debug_checks.store(enabled ? 1 : 0);
+  return prev;
+}
 
 const char* pa_status_string(int status) {
   switch (status) {
@@ -239,6 +286,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_DUPLICATE_SLOT: return "PA_ERR_DUPLICATE_SLOT";
     case PA_ERR_BLOCK_CONFLICT: return "PA_ERR_BLOCK_CONFLICT";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS";
+    case PA_ERR_PRECONDITION: return "PA_ERR_PRECONDITION";
     default: return "PA_ERR_UNKNOWN";
   }
 }
@@ -408,6 +456,13 @@ int pa_store_kv(const void* k_new, const void* v_new, const int32_t* slot_mappin
     a.n = num_tokens;
     a.num_slots = num_blocks * PA_BLOCK_SIZE;
     a.hkv = num_kv_heads;
+    if (debug_checks_on()) {
+      int flags = 0;
+      const hipError_t ce = pa::check_slots(slot_mapping, num_tokens, a.num_slots,
+                                            static_cast<hipStream_t>(stream), &flags);
+      if (ce != hipSuccess) return hip_fail(ce, "store_kv checks");
+      if (flags) return precondition_fail(flags);
+    }
     const hipError_t e = pa::launch_store_kv(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "store_kv launch");
     return ok();
@@ -531,6 +586,23 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
     char* wsb = static_cast<char*>(workspace);
     a.rec_ml = need > 0 ? reinterpret_cast<float*>(wsb) : nullptr;
     a.rec_o = need > 0 ? reinterpret_cast<float*>(wsb + ps.ml_bytes) : nullptr;
+    if (debug_checks_on()) {
+      pa::SeqCheckArgs c{};
+      c.ctx_lens = context_lens;
+      c.block_table = block_table;
+      c.cu_q = cu_seqlens_q;
+      c.num_blocks = num_blocks;
+      c.total_q = total_q_rows;
+      c.batch = batch;
+      c.mbps = max_blocks_per_seq;
+      c.max_context_len = int(std::min<int64_t>(int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE, INT32_MAX));
+      c.max_q = max_seqlen_q;
+      c.rows_per_seq = 1;
+      int flags = 0;
+      const hipError_t ce = pa::check_seqs(c, static_cast<hipStream_t>(stream), &flags);
+      if (ce != hipSuccess) return hip_fail(ce, "prefill checks");
+      if (flags) return precondition_fail(flags);
+    }
     const hipError_t e = pa::launch_prefill(a, group, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available");
     if (e != hipSuccess) return hip_fail(e, "prefill launch");

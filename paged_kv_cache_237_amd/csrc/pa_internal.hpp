@@ -112,6 +112,27 @@ __host__ __device__ constexpr int decode_group_waves(int g) { return g == 8 ? 4 
 // local); returns the status.
 int report_error(int code, const std::string& msg);
 
+// Device-side precondition checks (debug mode): bits of the violated
+// conditions, read back synchronously.
+constexpr int kCheckSlot = 1;   // a slot past the pool
+constexpr int kCheckCtx = 2;    // a context length outside [0, cap]
+constexpr int kCheckTable = 4;  // a used block-table entry outside the pool
+constexpr int kCheckRows = 8;   // cu_seqlens_q / rows per sequence inconsistent
+struct SeqCheckArgs {
+  const int32_t* ctx_lens;
+  const int32_t* block_table;
+  const int32_t* cu_q;  // varlen calls, else nullptr
+  int64_t num_blocks;
+  int64_t total_q;
+  int batch;
+  int mbps;
+  int max_context_len;
+  int max_q;
+  int rows_per_seq;     // decode: query rows per sequence
+};
+hipError_t check_slots(const int32_t* slots, int64_t n, int64_t num_slots, hipStream_t s, int* flags);
+hipError_t check_seqs(const SeqCheckArgs& a, hipStream_t s, int* flags);
+
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
