@@ -10,10 +10,18 @@
 // ceil(ctx/64) tiles of 64 tokens.  All segments are laid end to end and the
 // resulting list of tiles is cut into n_waves runs, one per wave, whose
 // lengths are set by the XCD the wave runs on (shorter on the slower,
-// odd-numbered XCDs), whatever the length mix.  A
-// workgroup holds the waves of one CU; the CU's waves share its bandwidth but
-// are not served evenly, so a wave that gets ahead of its slowest sibling
-// yields issue priority (s_setprio) and the CU's runs end together.
+// odd-numbered XCDs), whatever the length mix.  A workgroup holds the waves
+// of one CU; the CU's waves share its bandwidth but are not served evenly, so
+// a wave that gets ahead of its slowest sibling yields issue priority
+// (s_setprio) and the CU's runs end together.
+//
+// Several query rows per sequence (the causal decode of a few new tokens at
+// once): the ql rows x G heads of one (sequence, kv head) are the kernel's
+// "virtual heads" (G template = their count rounded up to a power of two);
+// virtual head v is query row v / G_real and sees the keys up to
+// ctx - ql + v / G_real, an additive mask per head.  With one row per
+// sequence (Causal = false) the mask and the general row addressing
+// compile away.
 //
 // A run streams its tiles as one software pipeline: the K loads of the next
 // tile are issued as soon as the current tile's scores are computed and its V
