@@ -2,9 +2,11 @@
  * pa.h -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
  *
  * C ABI of libpa.so: a slot-mapped store of new keys/values into a cache made
- * of fixed-size blocks, paged decode attention (one query token per sequence)
- * and causal varlen prefill attention over the same paged cache, plus whole-
- * block copies (copy-on-write inside a pool, swap between pools).
+ * of fixed-size blocks, paged decode attention (one query token per sequence,
+ * or a few with causal masking among them) and causal varlen prefill
+ * attention over the same paged cache, whole-block copies (copy-on-write
+ * inside a pool, swap between pools), and the host-side block manager that
+ * produces block tables and slot mappings.
  *
  * What the operations compute (no code is taken from these sources):
  *   - nano-vllm hub page (pomoai.com), section "Attention + Triton Kernel":
@@ -44,9 +46,11 @@
  *                 of a row are read.
  *
  * Memory and streams
- *   Every array argument is a DEVICE pointer owned by the caller (except the
- *   host array of pa_validate_slots).  The library allocates nothing, keeps no
- *   state beyond cached device attributes, and is thread-safe.  Every call is
+ *   Every array argument of a GPU call is a DEVICE pointer owned by the
+ *   caller (host arrays are marked as such: the validators, pa_swap_blocks'
+ *   pair list, the block manager).  The GPU calls allocate nothing; the
+ *   library keeps only cached device attributes and the debug-check switch,
+ *   and is thread-safe (a block manager serialises its own calls).  Every call is
  *   asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
  *   stream) on the current device.  The caller orders a store before the
  *   attention that reads it by issuing both on one stream.
@@ -58,9 +62,9 @@
  *   batch (num_tokens == 0, batch == 0) is a successful no-op.  No C++
  *   exception crosses the ABI.
  *
- * Data preconditions (not checked on the host; device code never reads or
- * writes outside the arrays whatever the data, but the affected outputs are
- * then unspecified):
+ * Data preconditions (not checked on the host -- pa_set_debug_checks turns on
+ * device-side checks of them; device code never reads or writes outside the
+ * arrays whatever the data, but the affected outputs are then unspecified):
  *   - slots are < num_blocks*block_size (a negative slot means "skip");
  *   - no two tokens of one pa_store_kv call share a slot;
  *   - block_table entries that are read lie in [0, num_blocks);

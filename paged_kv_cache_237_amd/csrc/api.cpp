@@ -1,16 +1,17 @@
 // C-ABI entry points of libpa: host-side argument checks, launch sizing and
 // error reporting.  Declarations and the contract of every call are in
-// include/pa.h.  Nothing here allocates device memory or keeps state beyond a
-// per-device cache of the compute-unit count.
+// include/pa.h.  Nothing here allocates device memory; the only state is a
+// per-device cache of the compute-unit count and the debug-check switch (the
+// host block manager in block_manager.cpp owns its own host memory).
 #include "pa.h"
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
-#include <atomic>
 #include <cstdlib>
 #include <mutex>
 #include <string>
