@@ -483,9 +483,8 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float x = acc[h][e];
-          x += __shfl_xor(x, 16, kWave);
-          x += __shfl_xor(x, 32, kWave);
-          acc[h][e] = x;
+          x = xor16_sum(x);
+          acc[h][e] = xor32_sum(x);
         }
         lsum[h] = wave_sum(l[h]);
       }

@@ -93,6 +93,32 @@ __device__ __forceinline__ int row16_sum_i(int x) {
   return x + dpp_i<kDppMirror>(x);
 }
 
+// x combined with the value of lane l^32 (or l^16) in VALU, with no LDS
+// round trip.  v_permlane32_swap exchanges lanes 32..63 of its first operand
+// with lanes 0..31 of its second; given x twice, the two results hold, in
+// every lane, x of lanes l%32 and l%32 + 32 -- the lane's own value and its
+// partner's, so a commutative combine of the two equals x_l op x_(l^32)
+// bit for bit.  v_permlane16_swap does the same for 16-lane rows 1, 3 against
+// rows 0, 2.  The results are copied to plain integers before use.
+__device__ __forceinline__ float xor32_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+
 // Wave-uniform max / sum of one value per lane.
 __device__ __forceinline__ float wave_max(float x) {
   x = row16_max(x);

@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[ms][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+    mt = xor32_max(mt) * c;
     const float mnew = fmaxf(m, mt);
     const bool need = mnew > m + kLazyRescale;  // also true for the first finite max
     if (__ballot(need) != 0) {
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     softmax_pv(t, s);
   }
 
-  const float ltot = l + __shfl_xor(l, 32, 64);
+  const float ltot = xor32_sum(l);
   if (nsplit > 1) {
     write_part<G>(a, g, part, q0, qlen, p0, o, m, ltot);
     return;
