@@ -97,27 +97,37 @@ __device__ __forceinline__ bool vreal(const DecodeArgs& a, int v) {
   return !Causal || (v >> a.gr_shift) < a.ql;
 }
 
-// Number of tiles of all segments (identical in every lane).
-__device__ int total_tiles(const DecodeArgs& a) {
+// Tiles per sequence of the first 64 sequences (lane = sequence), their
+// inclusive scan, and the number of tiles of all segments (identical in every
+// lane); `locate` reuses the first 64 from registers.
+struct TileScan {
+  int nt, incl, total;
+};
+
+__device__ TileScan scan_tiles(const DecodeArgs& a) {
   const int lane = lane_id();
-  int tot = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+  TileScan sc;
+  sc.nt = lane < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[lane])) : 0;
+  sc.incl = wave_incl_scan(sc.nt);
+  int tot = __builtin_amdgcn_readlane(sc.incl, kWave - 1);
+  for (int b0 = kWave; b0 < a.batch; b0 += kWave) {
     const int b = b0 + lane;
     const int nt = b < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[b])) : 0;
     tot += wave_sum_i(nt);
   }
-  return tot * a.hkv;
+  sc.total = tot * a.hkv;
+  return sc;
 }
 
 // Sequence holding tile `pos` of the flattened list and the tiles of all
 // sequences before it.
-__device__ void locate(const DecodeArgs& a, int pos, int& b_out, int& before_out) {
+__device__ void locate(const DecodeArgs& a, const TileScan& sc, int pos, int& b_out, int& before_out) {
   const int lane = lane_id();
   int base = 0;
   for (int b0 = 0; b0 < a.batch; b0 += kWave) {
     const int b = b0 + lane;
-    const int nt = b < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[b])) : 0;
-    const int incl = wave_incl_scan(nt);
+    const int nt = b0 == 0 ? sc.nt : (b < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[b])) : 0);
+    const int incl = b0 == 0 ? sc.incl : wave_incl_scan(nt);
     const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
     if (pos < (base + tot) * a.hkv) {
       const uint64_t hit = __ballot((base + incl) * a.hkv > pos);
@@ -295,7 +305,7 @@ __device__ __forceinline__ void issue_v(const TileLoads& tl, uint4 (&vr)[16]) {
 // partial record at seg + wave.  Returns the number of cut segments, whose
 // (b, g, first run, last run) are stored in pend_*.
 template <int G, bool Causal>
-__device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& runs, int wave, uint4* q_lds,
+__device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int end, const Runs& runs, int wave, uint4* q_lds,
                           float* p_lds, int* prog, int wv, int (&pend_b)[2], int (&pend_g)[2],
                           int (&pend_w0)[2], int (&pend_w1)[2]) {
   constexpr int NW = GroupShape<G>::kWaves;
@@ -304,7 +314,7 @@ __device__ int stream_run(const DecodeArgs& a, int pos, int end, const Runs& run
   constexpr int kQPerLane = (G * kChunks + kWave - 1) / kWave;
 
   int b, before;
-  locate(a, pos, b, before);
+  locate(a, sc, pos, b, before);
   if (b >= a.batch) return 0;
   int nt = tiles_of(clamp_ctx(a, a.ctx_lens[b]));
   const int off = pos - before * a.hkv;
@@ -565,21 +575,24 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   if (lane_id() == 0) prog[wv] = 0;
   __syncthreads();
 
-  // Empty contexts have no tiles: their output rows are zero.
-  if (wave < a.n_waves) {
+  // Empty contexts have no tiles: their output rows are zero.  Written on
+  // the way out, so that no wave waits for it before streaming.
+  auto zero_empty_rows = [&]() {
+    if (wave >= a.n_waves) return;
     for (int bb = wave; bb < a.batch; bb += a.n_waves) {
       if (clamp_ctx(a, a.ctx_lens[bb]) != 0) continue;
       uint32_t* o = reinterpret_cast<uint32_t*>(a.out + int64_t(bb) * a.ql * a.hq * kDim);
       for (int i = lane_id(); i < a.ql * a.hq * (kDim / 2); i += kWave) o[i] = 0u;
     }
-  }
+  };
 
-  const int total = total_tiles(a);
-  const Runs runs = make_runs<NW>(a, total);
+  const TileScan sc = scan_tiles(a);
+  const Runs runs = make_runs<NW>(a, sc.total);
   const int pos = run_start<NW>(runs, wave);
   const int end = run_start<NW>(runs, wave + 1);
   if (pos >= end) {
     if (lane_id() == 0) prog[wv] = 1 << 30;
+    zero_empty_rows();
     return;
   }
 
@@ -587,7 +600,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   // are counted once the whole run has been streamed, so the record stores
   // never stall the loads.
   int pend_b[2], pend_g[2], pend_w0[2], pend_w1[2];
-  const int npend = stream_run<G, Causal>(a, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
+  const int npend = stream_run<G, Causal>(a, sc, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
                                   pend_g, pend_w0, pend_w1);
   // a finished wave no longer holds its siblings back
   if (lane_id() == 0) prog[wv] = 1 << 30;
@@ -610,6 +623,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
       }
     }
   }
+  zero_empty_rows();
 }
 
 template <int G>

@@ -143,14 +143,22 @@ __device__ __forceinline__ int wave_max_i(int x) {
              max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
-// Inclusive prefix sum across the 64 lanes (lane i gets x_0 + ... + x_i).
+// Inclusive prefix sum across the 64 lanes (lane i gets x_0 + ... + x_i),
+// in DPP: shifts by 1, 2, 4, 8 within each 16-lane row (lanes shifted in from
+// outside the row read 0), then the last lane of row 0 / row 2 is added to
+// rows 1 / 3 (row_bcast:15) and the last lane of row 1 to rows 2 and 3
+// (row_bcast:31).  Disabled rows keep the `old` operand, 0.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1 + 1, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1 + 3, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1 + 7, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
   return x;
 }
 
