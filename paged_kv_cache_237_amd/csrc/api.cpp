@@ -561,7 +561,8 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
         return fail(PA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
                                           std::to_string(workspace_bytes));
     }
-    if (int64_t(batch) * ps.max_splits > int64_t(INT32_MAX) || 2 * int64_t(ps.nqb_max) > 65535)
+    if (int64_t(batch) * ps.max_splits > int64_t(INT32_MAX) || 2 * int64_t(ps.nqb_max) > 65535 ||
+        num_kv_heads > 65535)
       return fail(PA_ERR_BAD_SHAPE, "launch grid too large");
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(cu_seqlens_q, 4))

@@ -200,14 +200,34 @@ __device__ __forceinline__ int wave_of(const Runs& r, int tile) {
 }
 
 // Partial records cross XCDs (each XCD has its own L2), so they are written
-// and read with agent-scope atomic accesses, which the hardware keeps coherent
-// by themselves (no whole-L2 writeback or invalidate is needed, unlike a
-// device-scope fence).
+// and read at agent scope, which the hardware keeps coherent by itself (no
+// whole-L2 writeback or invalidate is needed, unlike a device-scope fence).
+// On gfx950 an agent-scope access is an ordinary one with the SC1 cache-policy
+// bit: single words go through relaxed agent-scope atomics, and the O vectors
+// through 16- and 8-byte buffer accesses that carry the same bit (a record is
+// padded to a multiple of 16 bytes), one transaction per chunk instead of one
+// per word.
+constexpr int kCpolAgent = 16;  // SC1 in the buffer builtins' cache-policy operand
+
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Four floats at byte offset off of the record (16-byte aligned).
+__device__ __forceinline__ void st_coherent4(__amdgpu_buffer_rsrc_t rec, uint32_t off, float x, float y,
+                                             float z, float w) {
+  const u32x4_t v = {__float_as_uint(x), __float_as_uint(y), __float_as_uint(z), __float_as_uint(w)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, rec, int(off), 0, kCpolAgent);
+}
+// Two floats at byte offset off of the record (8-byte aligned).
+__device__ __forceinline__ void ld_coherent2(__amdgpu_buffer_rsrc_t rec, uint32_t off, float& x, float& y) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rec, int(off), 0, kCpolAgent);
+  const unsigned lo = v.x, hi = v.y;
+  x = __uint_as_float(lo);
+  y = __uint_as_float(hi);
 }
 
 // Merge the partial records of segment `seg` written by waves w0..w1 into
@@ -228,12 +248,13 @@ __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0
     for (int j = 0; j < 4; ++j) {
       const bool have = w + j <= w1;
       const float* rec = a.ws + int64_t(seg + (have ? w + j : w0)) * partial_floats(G);
+      const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, uint32_t(partial_floats(G)) * 4u);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         mm[j][h] = have ? ld_coherent(rec + G * kDim + h) : -INFINITY;
         ll[j][h] = have ? ld_coherent(rec + G * kDim + G + h) : 0.f;
-        ua[j][h] = have ? ld_coherent(rec + h * kDim + 2 * lane) : 0.f;
-        ub[j][h] = have ? ld_coherent(rec + h * kDim + 2 * lane + 1) : 0.f;
+        ld_coherent2(rr, uint32_t(h * kDim + 2 * lane) * 4u, ua[j][h], ub[j][h]);
+        if (!have) ua[j][h] = ub[j][h] = 0.f;
       }
     }
 #pragma unroll
@@ -515,10 +536,13 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
         const int seg = b * a.hkv + g;
         float* rec = a.ws + int64_t(seg + wave) * partial_floats(G);
         if (lane < 16) {
+          const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, uint32_t(partial_floats(G)) * 4u);
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st_coherent(rec + h * kDim + lane * 8 + e, acc[h][e]);
+          for (int h = 0; h < G; ++h) {
+            const uint32_t off = uint32_t(h * kDim + lane * 8) * 4u;
+            st_coherent4(rr, off, acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            st_coherent4(rr, off + 16u, acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+          }
         }
         if (lane < G) {
           float mv = m[0], lv = lsum[0];

@@ -18,7 +18,7 @@ constexpr int kTile = 64;        // decode tile: one token per lane
 
 // Partial-state record of one decode work piece: G rows of D fp32 weighted
 // values, then G maxima, then G sums (floats).
-__host__ __device__ constexpr int partial_floats(int g) { return g * (kDim + 2); }
+__host__ __device__ constexpr int partial_floats(int g) { return (g * (kDim + 2) + 3) & ~3; }
 
 struct StoreArgs {
   const uint4* k_new;
