@@ -165,6 +165,39 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * pa_decode_append -- one decode step in one launch: the store of each
+ * sequence's new token and the decode attention over its context.
+ *
+ * For sequence b with n = context_lens[b] >= 1 (n counts the new token), the
+ * token at position n-1 is new: its rows k_new[b], v_new[b] are written into
+ * the caches at slot block_table[b][(n-1)/block_size]*block_size +
+ * (n-1)%block_size, and out[b] is pa_decode's result over positions 0 .. n-1
+ * with that position's key and value taken from k_new / v_new.  The result
+ * equals pa_store_kv (with those slots) followed by pa_decode, up to rounding
+ * order: positions 0 .. n-2 are read from the cache and the new token is
+ * folded in as one more partial state; nothing reads position n-1 of the
+ * cache during the call.  n == 0: a zero row and nothing stored.  A position
+ * whose block-table entry lies outside the pool contributes nothing and is
+ * not stored (as pa_decode and pa_store_kv treat such blocks).
+ *
+ *   k_new, v_new  : bf16 [batch][num_kv_heads][head_dim], 16-B aligned, not
+ *                   NULL when batch > 0.
+ *   k_cache, v_cache : the pools, written at the new positions.
+ *   workspace     : >= pa_decode_workspace_size(...) bytes; same rules as
+ *                   pa_decode's workspace.
+ *   Other arguments as for pa_decode.
+ *   Source: nano-vllm hub page, "Attention + Triton Kernel" (store through the
+ *   slot mapping, then attend) and "KV Cache block management" (the slot
+ *   formula); CSDN essay, first and third sections (the decode kernel).
+ */
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
  * pa_decode_multi -- decode of q_per_seq new tokens per sequence at once
  * (speculative verification: the drafted tokens and the next one scored in
  * one pass), each attending causally to the cache.

@@ -33,7 +33,8 @@ STATUS_NAMES = {
     -8: "PA_ERR_DUPLICATE_SLOT", -9: "PA_ERR_BLOCK_CONFLICT", -10: "PA_ERR_NO_BLOCKS", -11: "PA_ERR_PRECONDITION",
 }
 
-EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_multi_workspace_size",
+EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
+           "pa_decode_multi_workspace_size",
            "pa_decode_multi", "pa_prefill_workspace_size",
            "pa_prefill",
            "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         l.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_decode.restype = ctypes.c_int
+        l.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]
+        l.pa_decode_append.restype = ctypes.c_int
         l.pa_decode_multi_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
         l.pa_decode_multi_workspace_size.restype = _sz
         l.pa_decode_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
@@ -215,6 +219,29 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, max_context_len:
         raise ValueError("context_lens must be [B]")
     _check(lib().pa_decode(
         _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(k_cache, "k_cache", _BF16),
+        _dev(v_cache, "v_cache", _BF16), _dev(block_table, "block_table", _I32),
+        int(block_table.shape[1]), _dev(context_lens, "context_lens", _I32), b,
+        int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        _dev(workspace, "workspace", (torch.uint8, torch.float32, torch.int32)),
+        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+
+
+def decode_append(out, q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                  max_context_len: int, scale: float, workspace, stream=None) -> None:
+    """pa_decode_append: pa_decode whose newest position of each sequence is
+    the token k_new/v_new [B, Hkv, 128], which is also written into the
+    caches at that position (one launch for the store and the decode)."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    b, hq, d = (int(x) for x in q.shape)
+    if tuple(out.shape) != (b, hq, d) or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("shape mismatch between q, out and block_table")
+    if tuple(context_lens.shape) != (b,):
+        raise ValueError("context_lens must be [B]")
+    if tuple(k_new.shape) != (b, hkv, d) or tuple(v_new.shape) != (b, hkv, d):
+        raise ValueError("k_new and v_new must be [B, Hkv, 128]")
+    _check(lib().pa_decode_append(
+        _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(k_new, "k_new", _BF16),
+        _dev(v_new, "v_new", _BF16), _dev(k_cache, "k_cache", _BF16),
         _dev(v_cache, "v_cache", _BF16), _dev(block_table, "block_table", _I32),
         int(block_table.shape[1]), _dev(context_lens, "context_lens", _I32), b,
         int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale),

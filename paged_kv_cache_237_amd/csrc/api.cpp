@@ -179,12 +179,14 @@ int virtual_group(int group, int32_t q_per_seq) {
   return gv <= 8 ? gv : 0;
 }
 
-// Decode of q_per_seq query rows per sequence (1 for pa_decode).
-int decode_rows(void* out, const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                int32_t batch, int32_t q_per_seq, int32_t max_context_len, int32_t num_q_heads,
-                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                float scale, void* workspace, size_t workspace_bytes, void* stream) {
+// Decode of q_per_seq query rows per sequence (1 for pa_decode); with k_new
+// set (one row per sequence), the newest position of each sequence is the
+// appended token (pa_decode_append) and the caches are written.
+int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                const void* v_cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t batch, int32_t q_per_seq, int32_t max_context_len,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
     int group = 0;
@@ -205,6 +207,13 @@ int decode_rows(void* out, const void* q, const void* k_cache, const void* v_cac
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_table, 4) || !aligned(context_lens, 4))
       return fail(PA_ERR_ALIGN, "bf16 arrays must be 16-byte aligned, int32 arrays 4-byte");
+    const bool append = k_new != nullptr || v_new != nullptr;
+    if (append) {
+      if (!k_new || !v_new) return fail(PA_ERR_NULL_PTR, "pa_decode_append: k_new or v_new is NULL");
+      if (!aligned(k_new, 16) || !aligned(v_new, 16))
+        return fail(PA_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
+      if (q_per_seq != 1) return fail(PA_ERR_UNSUPPORTED, "an appended token needs one query row per sequence");
+    }
     // every tile index of the flattened work list must fit an int
     if (int64_t(batch) * num_kv_heads * max_blocks_per_seq * (PA_BLOCK_SIZE / pa::kTile) >
         int64_t(INT32_MAX) / 2)
@@ -241,6 +250,11 @@ int decode_rows(void* out, const void* q, const void* k_cache, const void* v_cac
     a.gr = group;
     a.gr_shift = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
     a.hq = num_q_heads;
+    a.k_new = static_cast<const uint4*>(k_new);
+    a.v_new = static_cast<const uint4*>(v_new);
+    // written only when a token is appended (the caller then passes writable caches)
+    a.k_store = append ? static_cast<uint4*>(const_cast<void*>(k_cache)) : nullptr;
+    a.v_store = append ? static_cast<uint4*>(const_cast<void*>(v_cache)) : nullptr;
     if (debug_checks_on()) {
       pa::SeqCheckArgs c{};
       c.ctx_lens = context_lens;
@@ -500,9 +514,22 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
               void* stream) {
-  return decode_rows(out, q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens, batch, 1,
-                     max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+  return decode_rows(out, q, nullptr, nullptr, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
+                     batch, 1, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                      workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (batch > 0 && (k_new == nullptr || v_new == nullptr))
+    return fail(PA_ERR_NULL_PTR, "pa_decode_append: k_new or v_new is NULL");
+  return decode_rows(out, q, k_new, v_new, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
+                     batch, 1, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     scale, workspace, workspace_bytes, stream);
 }
 
 int pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -511,8 +538,8 @@ int pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
                     int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_rows(out, q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens, batch,
-                     q_per_seq, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+  return decode_rows(out, q, nullptr, nullptr, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
+                     batch, q_per_seq, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, scale, workspace, workspace_bytes, stream);
 }
 

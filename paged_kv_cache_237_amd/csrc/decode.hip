@@ -23,6 +23,16 @@
 // sequence (Causal = false) the mask and the general row addressing
 // compile away.
 //
+// Appending the step's token (pa_decode_append): the newest position of each
+// sequence is not read from the cache.  The positions before it are streamed
+// as above; whichever wave finalises a (sequence, kv head) -- the one that
+// streamed it whole, the last one to arrive at its merge, or, for a context
+// of one token, the wave that writes its empty rows -- folds the new token in
+// as one more partial state (score q.k_new, weight 2^(score - M), value
+// v_new) and writes k_new / v_new into the cache at that position.  No wave
+// reads that position during the call, so the store needs no ordering; it
+// replaces the separate store launch of a decode step.
+//
 // A run streams its tiles as one software pipeline: the K loads of the next
 // tile are issued as soon as the current tile's scores are computed and its V
 // loads as soon as the current PV is done, also across segment boundaries
@@ -75,6 +85,13 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int n) {
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
 
+// Positions streamed from the cache: all of them, or all but the appended one.
+template <bool Append>
+__device__ __forceinline__ int stream_ctx(const DecodeArgs& a, int n) {
+  const int c = clamp_ctx(a, n);
+  return Append ? (c > 0 ? c - 1 : 0) : c;
+}
+
 // Load of a value the kernel never writes (block table, context lengths) at a
 // wave-uniform index, through the constant address space: it becomes a
 // scalar load, which is counted apart from the vector loads of K and V, so
@@ -104,15 +121,16 @@ struct TileScan {
   int nt, incl, total;
 };
 
+template <bool Append>
 __device__ TileScan scan_tiles(const DecodeArgs& a) {
   const int lane = lane_id();
   TileScan sc;
-  sc.nt = lane < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[lane])) : 0;
+  sc.nt = lane < a.batch ? tiles_of(stream_ctx<Append>(a, a.ctx_lens[lane])) : 0;
   sc.incl = wave_incl_scan(sc.nt);
   int tot = __builtin_amdgcn_readlane(sc.incl, kWave - 1);
   for (int b0 = kWave; b0 < a.batch; b0 += kWave) {
     const int b = b0 + lane;
-    const int nt = b < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[b])) : 0;
+    const int nt = b < a.batch ? tiles_of(stream_ctx<Append>(a, a.ctx_lens[b])) : 0;
     tot += wave_sum_i(nt);
   }
   sc.total = tot * a.hkv;
@@ -121,12 +139,13 @@ __device__ TileScan scan_tiles(const DecodeArgs& a) {
 
 // Sequence holding tile `pos` of the flattened list and the tiles of all
 // sequences before it.
+template <bool Append>
 __device__ void locate(const DecodeArgs& a, const TileScan& sc, int pos, int& b_out, int& before_out) {
   const int lane = lane_id();
   int base = 0;
   for (int b0 = 0; b0 < a.batch; b0 += kWave) {
     const int b = b0 + lane;
-    const int nt = b0 == 0 ? sc.nt : (b < a.batch ? tiles_of(clamp_ctx(a, a.ctx_lens[b])) : 0);
+    const int nt = b0 == 0 ? sc.nt : (b < a.batch ? tiles_of(stream_ctx<Append>(a, a.ctx_lens[b])) : 0);
     const int incl = b0 == 0 ? sc.incl : wave_incl_scan(nt);
     const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
     if (pos < (base + tot) * a.hkv) {
@@ -230,10 +249,60 @@ __device__ __forceinline__ void ld_coherent2(__amdgpu_buffer_rsrc_t rec, uint32_
   y = __uint_as_float(hi);
 }
 
+// The appended token of (sequence b, kv head g), position ctx-1: every lane
+// holds 16-byte chunk (lane & 15) of its K and V rows.  ok is false when the
+// sequence is empty or the position's block-table entry lies outside the
+// pool: the token then neither counts nor is stored (a block outside the pool
+// is masked in pa_decode too).  new_token_load only issues the loads (their
+// addresses depend on b and g alone), so callers start it early and use the
+// rows later; new_token_store writes them into the cache (lanes 0..15).
+struct NewToken {
+  bool ok;
+  int phys, row;
+  uint4 kc, vc;
+};
+
+__device__ __forceinline__ NewToken new_token_load(const DecodeArgs& a, int b, int g) {
+  const int j = lane_id() & 15;
+  const int64_t src = (int64_t(b) * a.hkv + g) * kChunks + j;
+  NewToken tk;
+  tk.kc = a.k_new[src];
+  tk.vc = a.v_new[src];
+  const int c = clamp_ctx(a, ld_uniform(a.ctx_lens, b));
+  const int p = c - 1;
+  tk.phys = c >= 1 ? ld_uniform(a.block_table, int64_t(b) * a.mbps + p / kBlock) : -1;
+  tk.row = p % kBlock;
+  tk.ok = tk.phys >= 0 && int64_t(tk.phys) < a.num_blocks;
+  return tk;
+}
+
+__device__ __forceinline__ void new_token_store(const DecodeArgs& a, const NewToken& tk, int g) {
+  const int lane = lane_id();
+  if (tk.ok && lane < 16) {
+    const int64_t bh = int64_t(tk.phys) * a.hkv + g;
+    a.k_store[(bh * kChunks + lane) * kBlock + tk.row] = tk.kc;
+    a.v_store[(bh * kBlock + tk.row) * kChunks + lane] = tk.vc;
+  }
+}
+
+__device__ __forceinline__ NewToken new_token(const DecodeArgs& a, int b, int g) {
+  const NewToken tk = new_token_load(a, b, g);
+  new_token_store(a, tk, g);
+  return tk;
+}
+
+// Score (log2 units) of a query against the appended key, given the lane's
+// chunk (lane & 15) of each: every 16-lane row of the wave sums the 16 chunk
+// products, so every lane gets the score.
+__device__ __forceinline__ float new_token_score(const DecodeArgs& a, const uint4& qc, const uint4& kc) {
+  return row16_sum(dot8_bf16(qc, kc, 0.f)) * a.scale_log2;
+}
+
 // Merge the partial records of segment `seg` written by waves w0..w1 into
 // its G output rows (lane = 2 dims).  One pass with an online rescale; the
-// loads of four records are issued together.
-template <int G, bool Causal>
+// loads of four records are issued together.  With Append, the new token is
+// folded in last.
+template <int G, bool Causal, bool Append>
 __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0, int w1) {
   const int lane = lane_id();
   float M[G], L[G], U0[G], U1[G];
@@ -241,6 +310,17 @@ __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0
   for (int h = 0; h < G; ++h) {
     M[h] = -INFINITY;
     L[h] = U0[h] = U1[h] = 0.f;
+  }
+  // the appended token's rows and the queries' chunks, loaded under the records
+  NewToken tk;
+  uint4 qc[G];
+  uint32_t vw = 0u;
+  if constexpr (Append) {
+    tk = new_token_load(a, b, g);
+    vw = reinterpret_cast<const uint32_t*>(a.v_new + (int64_t(b) * a.hkv + g) * kChunks)[lane];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      qc[h] = reinterpret_cast<const uint4*>(a.q + vrow<G, Causal>(a, b, g, h) * kDim)[lane & 15];
   }
   for (int w = w0; w <= w1; w += 4) {
     float mm[4][G], ll[4][G], ua[4][G], ub[4][G];
@@ -270,6 +350,23 @@ __device__ void merge_segment(const DecodeArgs& a, int seg, int b, int g, int w0
         U1[h] = U1[h] * sa + ub[j][h] * sb;
         M[h] = mn;
       }
+  }
+  if constexpr (Append) {
+    new_token_store(a, tk, g);
+    if (tk.ok) {
+      const float v0 = bf16_lo(vw), v1 = bf16_hi(vw);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float sn = new_token_score(a, qc[h], tk.kc);
+        const float mn = fmaxf(M[h], sn);
+        const float sa = __builtin_amdgcn_exp2f(M[h] - mn);
+        const float sb = __builtin_amdgcn_exp2f(sn - mn);
+        L[h] = L[h] * sa + sb;
+        U0[h] = U0[h] * sa + v0 * sb;
+        U1[h] = U1[h] * sa + v1 * sb;
+        M[h] = mn;
+      }
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -325,7 +422,7 @@ __device__ __forceinline__ void issue_v(const TileLoads& tl, uint4 (&vr)[16]) {
 // fold of the row partials and either the bf16 output (whole segment) or a
 // partial record at seg + wave.  Returns the number of cut segments, whose
 // (b, g, first run, last run) are stored in pend_*.
-template <int G, bool Causal>
+template <int G, bool Causal, bool Append>
 __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int end, const Runs& runs, int wave, uint4* q_lds,
                           float* p_lds, int* prog, int wv, int (&pend_b)[2], int (&pend_g)[2],
                           int (&pend_w0)[2], int (&pend_w1)[2]) {
@@ -335,13 +432,13 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
   constexpr int kQPerLane = (G * kChunks + kWave - 1) / kWave;
 
   int b, before;
-  locate(a, sc, pos, b, before);
+  locate<Append>(a, sc, pos, b, before);
   if (b >= a.batch) return 0;
-  int nt = tiles_of(clamp_ctx(a, a.ctx_lens[b]));
+  int nt = tiles_of(stream_ctx<Append>(a, a.ctx_lens[b]));
   const int off = pos - before * a.hkv;
   int g = off / nt;
   int t = off - g * nt;
-  int ctx = clamp_ctx(a, a.ctx_lens[b]);
+  int ctx = stream_ctx<Append>(a, a.ctx_lens[b]);
   b = __builtin_amdgcn_readfirstlane(b);
   g = __builtin_amdgcn_readfirstlane(g);
   t = __builtin_amdgcn_readfirstlane(t);
@@ -390,12 +487,14 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
         nctx = 0;
         do {
           nb = __builtin_amdgcn_readfirstlane(nb + 1);
-          nctx = nb < a.batch ? clamp_ctx(a, ld_uniform(a.ctx_lens, nb)) : 0;
+          nctx = nb < a.batch ? stream_ctx<Append>(a, ld_uniform(a.ctx_lens, nb)) : 0;
           nnt = nb < a.batch ? tiles_of(nctx) : 1;
         } while (nnt == 0);
       }
     }
     const bool next_ok = has_next && nb < a.batch;
+    // the appended token of a segment this wave finishes whole: its rows are
+    // loaded under the segment's last tile
     uint4 qn[kQPerLane];
     if (seg_end && next_ok) {
       if constexpr (!Causal) {
@@ -520,6 +619,25 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
         lsum[h] = wave_sum(l[h]);
       }
       if (piece_t0 == 0 && seg_end) {
+        if constexpr (Append) {
+          // lane holds dims 8*(lane & 15) .. +7 of every head; q is still
+          // this segment's in LDS
+          const NewToken tk = new_token(a, b, g);
+          if (tk.ok) {
+            float vn[8];
+            unpack8(tk.vc, vn);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float sn = new_token_score(a, q_lds[h * kChunks + (lane & 15)], tk.kc);
+              const float mn = fmaxf(m[h], sn);
+              const float sa = __builtin_amdgcn_exp2f(m[h] - mn);
+              const float sb = __builtin_amdgcn_exp2f(sn - mn);
+              lsum[h] = lsum[h] * sa + sb;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * sa + vn[e] * sb;
+            }
+          }
+        }
         if (lane < 16) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
@@ -588,7 +706,7 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
   return npend;
 }
 
-template <int G, bool Causal>
+template <int G, bool Causal, bool Append>
 __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = GroupShape<G>::kWaves;
   __shared__ uint4 q_lds[NW][G * kChunks];
@@ -599,18 +717,31 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   if (lane_id() == 0) prog[wv] = 0;
   __syncthreads();
 
-  // Empty contexts have no tiles: their output rows are zero.  Written on
-  // the way out, so that no wave waits for it before streaming.
+  // Empty contexts have no tiles: their output rows are zero.  With Append,
+  // a context of one token streams nothing either: its rows are that token's
+  // V (the softmax of a single score is 1), and the token is stored here.
+  // Written on the way out, so that no wave waits for it before streaming.
   auto zero_empty_rows = [&]() {
     if (wave >= a.n_waves) return;
     for (int bb = wave; bb < a.batch; bb += a.n_waves) {
-      if (clamp_ctx(a, a.ctx_lens[bb]) != 0) continue;
+      const int c = clamp_ctx(a, ld_uniform(a.ctx_lens, bb));
+      if (Append && c == 1) {
+        for (int gg = 0; gg < a.hkv; ++gg) {
+          const NewToken tk = new_token(a, bb, gg);
+          if (lane_id() < 16) {
+            uint4* o = reinterpret_cast<uint4*>(a.out + (int64_t(bb) * a.hq + int64_t(gg) * a.gr) * kDim);
+            for (int hh = 0; hh < a.gr; ++hh) o[hh * kChunks + lane_id()] = tk.ok ? tk.vc : make_uint4(0u, 0u, 0u, 0u);
+          }
+        }
+        continue;
+      }
+      if (c != 0) continue;
       uint32_t* o = reinterpret_cast<uint32_t*>(a.out + int64_t(bb) * a.ql * a.hq * kDim);
       for (int i = lane_id(); i < a.ql * a.hq * (kDim / 2); i += kWave) o[i] = 0u;
     }
   };
 
-  const TileScan sc = scan_tiles(a);
+  const TileScan sc = scan_tiles<Append>(a);
   const Runs runs = make_runs<NW>(a, sc.total);
   const int pos = run_start<NW>(runs, wave);
   const int end = run_start<NW>(runs, wave + 1);
@@ -624,7 +755,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
   // are counted once the whole run has been streamed, so the record stores
   // never stall the loads.
   int pend_b[2], pend_g[2], pend_w0[2], pend_w1[2];
-  const int npend = stream_run<G, Causal>(a, sc, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
+  const int npend = stream_run<G, Causal, Append>(a, sc, pos, end, runs, wave, q_lds[wv], p_lds[wv], prog, wv, pend_b,
                                   pend_g, pend_w0, pend_w1);
   // a finished wave no longer holds its siblings back
   if (lane_id() == 0) prog[wv] = 1 << 30;
@@ -641,7 +772,7 @@ __global__ __launch_bounds__(GroupShape<G>::kThreads) void decode_split_kernel(D
         prev = __hip_atomic_fetch_add(a.counters + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = __builtin_amdgcn_readfirstlane(prev);
       if (prev == pend_w1[i] - pend_w0[i]) {
-        merge_segment<G, Causal>(a, seg, pend_b[i], pend_g[i], pend_w0[i], pend_w1[i]);
+        merge_segment<G, Causal, Append>(a, seg, pend_b[i], pend_g[i], pend_w0[i], pend_w1[i]);
         if (lane_id() == 0)
           __hip_atomic_store(a.counters + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -654,11 +785,19 @@ template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
   constexpr int NW = GroupShape<G>::kWaves;
   const unsigned split_blocks = unsigned((a.n_waves + NW - 1) / NW);
-  // one query row per sequence needs no causal mask inside the context
-  if (a.ql == 1)
-    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0, s, a);
+  // one query row per sequence needs no causal mask inside the context; the
+  // appended token is supported with one query row only
+  if (a.k_new != nullptr) {
+    if (a.ql != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_split_kernel<G, false, true>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0,
+                       s, a);
+  } else if (a.ql == 1) {
+    hipLaunchKernelGGL((decode_split_kernel<G, false, false>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0,
+                       s, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<G, true, false>), dim3(split_blocks), dim3(GroupShape<G>::kThreads), 0,
+                       s, a);
+  }
   return hipGetLastError();
 }
 

@@ -57,6 +57,15 @@ struct DecodeArgs {
   int gr;
   int gr_shift;
   int hq;
+  // Appended token (one query row per sequence only): when k_new is set, the
+  // token at position ctx-1 of every sequence is new.  Its K/V rows
+  // k_new/v_new [batch][hkv][kDim] take part in the attention directly (the
+  // kernel streams positions 0 .. ctx-2 from the cache) and are written into
+  // the cache at that position through the block table.
+  const uint4* k_new;
+  const uint4* v_new;
+  uint4* k_store;
+  uint4* v_store;
 };
 
 struct PrefillArgs {
