@@ -49,9 +49,17 @@ def store_bytes(n_tokens: int, hkv: int, d: int = 128) -> int:
     return 2 * n_tokens * hkv * d * 2 * 2 + 4 * n_tokens
 
 
+def append_bytes(case: wl.PagedCase) -> int:
+    """Algorithmic bytes of one pa_decode_append: those of pa_decode (the new
+    token's K and V rows come from k_new / v_new instead of the cache, the
+    same bytes) plus the new rows written into the cache."""
+    n_new = int((case.context_lens > 0).sum())
+    return decode_bytes(case) + n_new * case.num_kv_heads * case.head_dim * 2 * 2
+
+
 def place(case):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from paged_harness import place as _place  # noqa: E402
+    from device_case import place as _place  # noqa: E402
     return _place(case)
 
 
@@ -67,82 +75,110 @@ def copy_probe(mib: int) -> None:
     del src, dst
 
 
-def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True):
-    """Times `steps` decode steps (store of the new tokens + decode) after
-    `warmup`; returns (ms_per_step, decode_ms_avg, store_ms_avg).
+def new_rows(dev):
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from device_case import new_rows as _new_rows  # noqa: E402
+    return _new_rows(dev)
 
-    ms_per_step: the step captured once in a HIP graph and replayed `steps`
-    times (a serving loop replays its step; this removes host launch gaps),
-    or eager launches with graph=False.  decode_ms / store_ms: HIP events
-    around each call in a separate eager loop, on the stream the kernels run
-    on."""
+
+def _graph_of(fn):
+    """fn captured once in a HIP graph (after a warm-up call on the capture
+    stream)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _events_ms(fn, steps, before=None):
+    """Mean and list of HIP-event times (ms) of `steps` eager calls of fn, on
+    the stream the kernels run on; `before` runs outside the events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if before is not None:
+            before()
+        a.record(torch.cuda.current_stream())
+        fn()
+        b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ts)), ts
+
+
+def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True) -> dict:
+    """Times `steps` decode steps after `warmup`.  A step stores each
+    sequence's new token and attends over the whole context; it runs as one
+    pa_decode_append launch ("step_ms", the headline) and, for comparison, as
+    pa_store_kv + pa_decode ("two_call_step_ms").  Whole steps are captured
+    once in a HIP graph and replayed (a serving loop replays its step; this
+    removes host launch gaps), or launched eagerly with graph=False.  Kernel
+    times ("append_ms", "decode_ms", "store_ms") are HIP events around single
+    eager calls on the stream the kernels run on; "decode_ms_flushed" are
+    pa_decode times with the caches (4 MB L2 per XCD, 256 MB MALL) flushed
+    before each call by reading 1 GiB of other data, outside the events: what
+    one layer of a deep model sees, since its cache is read again only after
+    every other layer's (a read leaves clean lines; a write-based flush would
+    also charge the decode with writing back 256 MB of dirty lines).  Every
+    call writes the same token bytes to the same slots, so the cache state is
+    the same for all of them."""
     dev = place(case)
+    k_new, v_new = new_rows(dev)
     out = torch.empty((case.batch, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
                       device="cuda")
     ws = pa.alloc_decode_workspace(case.batch, case.num_q_heads, case.num_kv_heads)
 
-    def step(ev=None):
-        stream = torch.cuda.current_stream()
-        if ev is not None:
-            ev[0].record(stream)
+    def store():
         pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def decode():
         pa.decode(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens,
                   case.max_context_len, case.scale, ws)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def append():
+        pa.decode_append(out, dev.q, k_new, v_new, dev.k_cache, dev.v_cache, dev.block_table,
+                         dev.context_lens, case.max_context_len, case.scale, ws)
+
+    def two_calls():
+        store()
+        decode()
 
     for _ in range(warmup):
-        step()
-    # per-kernel events (eager)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    dec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    sto = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    # The same with the caches (4 MB L2 per XCD, 256 MB MALL) flushed between
-    # calls by reading 1 GiB of other data, outside the events: what one layer
-    # of a deep model sees, since its cache is read again only after every
-    # other layer's.  A read leaves clean lines; a write-based flush would
-    # also charge the decode with writing back 256 MB of dirty lines.
+        two_calls()
+        append()
+    res = {}
+    res["append_ms"], _ = _events_ms(append, steps)
+    res["store_ms"], _ = _events_ms(store, steps)
+    res["decode_ms"], _ = _events_ms(decode, steps)
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        torch.amax(flush, dim=0, out=sink)
-        step(evf[i])
-    torch.cuda.synchronize()
-    dec_flushed = [e[1].elapsed_time(e[2]) for e in evf]
+    _, res["decode_ms_flushed"] = _events_ms(decode, steps,
+                                             before=lambda: torch.amax(flush, dim=0, out=sink))
     del flush, sink
 
-    # whole steps
-    if graph:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step()
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=s):
-                step()
-        torch.cuda.synchronize()
+    def whole(fn):
+        run = _graph_of(fn).replay if graph else fn
         for _ in range(warmup):
-            g.replay()
-        run = g.replay
-    else:
-        run = step
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    res["two_call_step_ms"] = whole(two_calls)
+    res["step_ms"] = whole(append)
     del dev
     torch.cuda.empty_cache()
-    return wall * 1e3 / steps, dec, sto, dec_flushed
+    return res
 
 
 def prefill_flops(case: wl.PagedCase) -> int:
@@ -542,14 +578,17 @@ def main(argv=None):
         return 2
     print(f"[bench] {case.name}: B={case.batch} sum_ctx={int(case.context_lens.sum())}",
           file=sys.stderr, flush=True)
-    ms_step, dec_ms, sto_ms, dec_flushed = time_decode(case, args.steps, args.warmup,
-                                                       graph=not args.no_graph)
+    t = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
     copy_probe(args.copy_probe_mib)
     dbytes = decode_bytes(case)
     sbytes = store_bytes(case.batch, case.num_kv_heads)
+    abytes = append_bytes(case)
     sum_ctx = int(case.context_lens.sum())
+    ms_step = t["step_ms"]
     step_gbs = (dbytes + sbytes) / (ms_step * 1e-3) / 1e9
-    dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    app_gbs = abytes / (t["append_ms"] * 1e-3) / 1e9
+    dec_gbs = dbytes / (t["decode_ms"] * 1e-3) / 1e9
+    flushed = t["decode_ms_flushed"]
     line = {
         "metric": METRIC,
         "value": round(step_gbs, 1),
@@ -570,28 +609,46 @@ def main(argv=None):
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "attended_tokens_per_s": round(sum_ctx / (ms_step * 1e-3), 1),
-        "step_launch": "hip graph replay" if not args.no_graph else "eager",
-        "decode_ms": round(dec_ms, 4),
-        "decode_ms_caches_flushed": {"median": round(float(np.median(dec_flushed)), 4),
-                                     "min": round(float(np.min(dec_flushed)), 4),
-                                     "max": round(float(np.max(dec_flushed)), 4)},
-        "store_ms": round(sto_ms, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel (pa_decode: split-context streaming with fused merge)",
-                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(case.name),
-                     "algorithmic_bytes_per_launch": dbytes},
+        "step_launch": ("one pa_decode_append launch (store of the new tokens + decode), "
+                        + ("hip graph replay" if not args.no_graph else "eager")),
+        "two_call_step": {"ms": round(t["two_call_step_ms"], 4),
+                          "GBps": round((dbytes + sbytes) / (t["two_call_step_ms"] * 1e-3) / 1e9, 1),
+                          "calls": "pa_store_kv + pa_decode"},
+        "append_ms": round(t["append_ms"], 4),
+        "decode_ms": round(t["decode_ms"], 4),
+        "decode_ms_caches_flushed": {"median": round(float(np.median(flushed)), 4),
+                                     "min": round(float(np.min(flushed)), 4),
+                                     "max": round(float(np.max(flushed)), 4)},
+        "store_ms": round(t["store_ms"], 4),
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_split_kernel<2, false, true> (pa_decode_append: the step's "
+                               "store and split-context decode with fused merge)",
+                     "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(case.name),
+                     "algorithmic_bytes_per_launch": abytes},
+        "pa_decode_roofline": {"kernel": "decode_split_kernel<2, false, false> (pa_decode)",
+                               "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes_per_launch": dbytes},
     }
     if not args.no_extra:
         extra = {}
         for name in ("qwen3_4b_decode", "long_context_decode"):
             c = wl.CONFIGS[name]()
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
-            m, d, s, dfl = time_decode(c, max(10, args.steps // 5), 3)
-            b = decode_bytes(c)
+            tc = time_decode(c, max(10, args.steps // 5), 3)
+            b, d = decode_bytes(c), tc["decode_ms"]
+            sb = store_bytes(c.batch, c.num_kv_heads)
             extra[name] = {"decode_ms": round(d, 4), "decode_GBps": round(b / (d * 1e-3) / 1e9, 1),
-                           "decode_ms_caches_flushed_median": round(float(np.median(dfl)), 4),
+                           "decode_ms_caches_flushed_median": round(float(np.median(tc["decode_ms_flushed"])), 4),
                            "frac_of_hbm_peak": round(b / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "attended_tokens_per_s": round(int(c.context_lens.sum()) / (d * 1e-3), 1),
+                           "append_ms": round(tc["append_ms"], 4),
+                           "append_frac_of_hbm_peak": round(append_bytes(c) / (tc["append_ms"] * 1e-3) / 1e9
+                                                            / HBM_PEAK_GBS, 4),
+                           "step_ms": round(tc["step_ms"], 4),
+                           "step_GBps": round((b + sb) / (tc["step_ms"] * 1e-3) / 1e9, 1),
+                           "two_call_step_ms": round(tc["two_call_step_ms"], 4),
                            "sum_context_len": int(c.context_lens.sum())}
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(10, args.steps // 5), 3)
