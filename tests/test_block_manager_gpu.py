@@ -6,7 +6,9 @@ copy-on-write pairs applied with pa_copy_blocks before the new tokens are
 stored), a sequence is freed and a new one reuses its blocks.  After every
 step the paged decode over the manager's block tables must equal, to the
 attention bar, the float64 oracle's attention over each sequence's logical
-token list -- which knows nothing of blocks, slots or copies."""
+token list -- which knows nothing of blocks, slots or copies.  A second run
+of the same sequence makes every decode step one pa_decode_append launch
+(the store left to the kernel, at the slot it derives from the table)."""
 
 import numpy as np
 import pytest
@@ -58,7 +60,11 @@ class Serving:
         self.bm.free(seq)
         del self.tokens[seq]
 
-    def append_all(self, batched):
+    def append_all(self, batched, fused=False):
+        """One token per sequence.  fused: the store is left to
+        pa_decode_append (decode_and_check), which writes each token at the
+        slot its block table gives for the newest position; the manager's
+        slot for that token must be the same one."""
         ids, slots, pairs = [], [], []
         seqs = sorted(self.tokens)
         if batched:
@@ -77,13 +83,17 @@ class Serving:
         if pairs:
             self.copies += len(pairs)
             pa.copy_blocks(self.k, self.v, torch.as_tensor(np.asarray(pairs, np.int32)).cuda())
-        self._store(ids, slots)
+        if fused:
+            self.pending = (ids, slots)
+        else:
+            self._store(ids, slots)
 
-    def decode_and_check(self, step):
+    def decode_and_check(self, step, fused=False):
         seqs = sorted(self.tokens)
         lens = [len(self.tokens[s]) for s in seqs]
         width = max(max(-(-n // pa.BLOCK_SIZE) for n in lens), 1)
-        table = torch.from_numpy(self.bm.block_table(seqs, width)).cuda()
+        tab = self.bm.block_table(seqs, width)
+        table = torch.from_numpy(tab).cuda()
         ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
         w = HQ * D
         q = wl.normal_bf16(SEED, wl.STREAM_Q, step * len(seqs) * w, len(seqs) * w)
@@ -91,7 +101,17 @@ class Serving:
         out = torch.empty((len(seqs), HQ, D), dtype=torch.bfloat16, device="cuda")
         ws = pa.alloc_decode_workspace(len(seqs), HQ, HKV)
         scale = D ** -0.5
-        pa.decode(out, q.cuda(), self.k, self.v, table, ctx, max(lens), scale, ws)
+        if fused:
+            ids, slots = self.pending
+            for n, row, slot in zip(lens, tab, slots):
+                p = n - 1
+                assert slot == int(row[p // pa.BLOCK_SIZE]) * pa.BLOCK_SIZE + p % pa.BLOCK_SIZE
+            k_new = torch.cat([token_rows(wl.STREAM_K, i, 1) for i in ids]).cuda()
+            v_new = torch.cat([token_rows(wl.STREAM_V, i, 1) for i in ids]).cuda()
+            pa.decode_append(out, q.cuda(), k_new, v_new, self.k, self.v, table, ctx, max(lens),
+                             scale, ws)
+        else:
+            pa.decode(out, q.cuda(), self.k, self.v, table, ctx, max(lens), scale, ws)
         torch.cuda.synchronize()
         ref = np.zeros((len(seqs), HQ, D))
         qf = oracle.bf16_to_f64(wl.bits_to_numpy(q))
@@ -128,3 +148,26 @@ def test_manager_driven_steps_match_attention_over_logical_tokens():
     seqs = sorted(sv.tokens)
     used = set(sv.bm.block_table(seqs, 4).ravel().tolist()) - {-1}
     assert used == set(range(14))
+
+
+def test_manager_driven_steps_with_the_one_launch_step():
+    """The same serving sequence with every decode step run as one
+    pa_decode_append launch: the manager's slot of each new token is the
+    slot the kernel derives from the block table, copy-on-write copies come
+    first, and the outputs match attention over the logical tokens; the
+    tokens the fused calls stored are read back by the next steps."""
+    print(f"[block manager, pa_decode_append] seed={SEED}", flush=True)
+    sv = Serving(num_blocks=14)
+    for seq, n in [(0, 300), (1, 256), (2, 700), (3, 1)]:
+        sv.prompt(seq, n)
+    sv.fork(0, 10)
+    sv.fork(2, 11)
+    sv.fork(1, 12)
+    for step in range(4):
+        sv.append_all(batched=step % 2 == 0, fused=True)
+        sv.decode_and_check(step, fused=True)
+        if step == 1:
+            sv.free(0)
+            sv.prompt(20, 1000)
+    assert sv.copies == 2
+    assert sv.bm.num_free == 0
