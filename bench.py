@@ -1,7 +1,8 @@
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-One step = the whole path over one batch: pa_store_kv of each sequence's new
-token, then pa_decode over every sequence's full paged context.  The default
+One step = the whole path over one batch: each sequence's new token is
+stored into its slot and attended together with its full paged context, as
+one pa_decode_append launch (pa_store_kv + pa_decode is timed beside it).  The default
 workload is the Qwen3-0.6B-shaped decode layer (batch 64, context lengths
 uniform on 512..4096, 16 query / 8 kv heads, head dim 128, 256-token blocks,
 physical blocks shuffled, pool +10 %).  Inputs are seeded synthetic data
@@ -94,6 +95,24 @@ def _graph_of(fn):
             fn()
     torch.cuda.synchronize()
     return g
+
+
+def _warm(fn, warmup: int, min_s: float = 0.2) -> None:
+    """Calls fn at least `warmup` times and for at least min_s seconds of
+    sustained GPU work.  The compute clock ramps up over the first ~50 ms of
+    sustained matrix work (prefill calls run ~180 us at first and ~160 us
+    after that; after two idle seconds the ramp starts over), so a warm-up
+    of a few calls would time the ramp, not the kernel.  Memory-bound decode
+    runs at its steady time from the first call."""
+    n = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def _events_ms(fn, steps, before=None):
@@ -217,8 +236,7 @@ def time_prefill(case: wl.PagedCase, steps: int, warmup: int):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(warmup):
-        step()
+    _warm(step, warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -241,7 +259,8 @@ def prefill_report(steps: int, warmup: int) -> dict:
             "prefill_TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
             "store_ms": round(sto, 4), "store_tokens": c.total_kv_rows,
             "store_GBps": round(sb / (sto * 1e-3) / 1e9, 1),
-            "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "rocprof_counters": recorded_prefill_counters()}
 
 
 def varlen_report(name: str, steps: int, warmup: int) -> dict:
@@ -278,8 +297,7 @@ def decode_multi_report(steps: int, warmup: int) -> dict:
         pa.decode_multi(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens, ql,
                         c.max_context_len, c.scale, ws)
 
-    for _ in range(warmup):
-        call()
+    _warm(call, warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
@@ -393,9 +411,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", "decode.hip")
 
 
-def source_digest(path: str) -> str:
+def source_digest(*paths: str) -> str:
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _read_csv(path: str):
@@ -483,6 +504,72 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key:
     return res
 
 
+# the prefill kernel and the device headers it includes
+PREFILL_SRC = tuple(os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", f)
+                    for f in ("prefill.hip", "pa_device.hpp", "pa_internal.hpp"))
+PREFILL_COUNTERS = os.path.join(PROFILES, "prefill_8x2048_sq_counters.json")
+
+
+def summarize_counters(out_md: str, kernel_key: str, csvs, commands) -> dict:
+    """SQ / GRBM counters of the kernel whose name contains kernel_key,
+    averaged over its dispatches (each value summed over the hardware
+    instances), from one or more rocprofv3 --pmc counter CSVs; writes a
+    Markdown table next to a JSON copy and returns the figures.  MFMA busy
+    fraction = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per XCD),
+    with GRBM_GUI_ACTIVE taken from the same pass."""
+    per_pass = []
+    for path in csvs:
+        vals = {}
+        for r in _read_csv(path):
+            if kernel_key not in r.get("Kernel_Name", ""):
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel matching {kernel_key!r} in {path}")
+        per_pass.append({k: (sum(v) / len(v), len(v)) for k, v in vals.items()})
+    merged = {}
+    for d in per_pass:
+        for k, (v, n) in d.items():
+            merged.setdefault(k, (v, n))
+    simds = 256 * 4
+    xcds = 8
+    ratios = {}
+    for d in per_pass:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d:
+            busy = d["SQ_VALU_MFMA_BUSY_CYCLES"][0]
+            ratios["mfma_busy_frac"] = busy / (simds * d["GRBM_GUI_ACTIVE"][0] / xcds)
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in d:
+                ratios["valu_coexec_frac_of_mfma_busy"] = d["SQ_VALU_MFMA_COEXEC_CYCLES"][0] / busy
+        if "SQ_WAIT_INST_ANY" in d and "SQ_WAVE_CYCLES" in d:
+            ratios["wait_inst_any_frac_of_wave_cycles"] = d["SQ_WAIT_INST_ANY"][0] / d["SQ_WAVE_CYCLES"][0]
+        if "SQ_WAIT_INST_LDS" in d and "SQ_WAVE_CYCLES" in d:
+            ratios["wait_inst_lds_frac_of_wave_cycles"] = d["SQ_WAIT_INST_LDS"][0] / d["SQ_WAVE_CYCLES"][0]
+    res = {"kernel_key": kernel_key, "counters": {k: v for k, (v, _) in sorted(merged.items())},
+           "dispatches": min(n for _, n in merged.values()), "ratios": ratios,
+           "prefill_source_sha256_16": source_digest(*PREFILL_SRC), "commands": list(commands)}
+    lines = [f"# `{kernel_key}` SQ counters", "",
+             "Commands (run from the repository root, one pass each; values are summed over the "
+             "hardware instances and averaged over the kernel's dispatches):", "", "```",
+             *commands, "```", "", "| counter | per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {v:.4g} |" for k, v in res["counters"].items()]
+    lines += ["", "| ratio | value |", "|---|---|"]
+    lines += [f"| {k} | {v:.3f} |" for k, v in ratios.items()]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    json.dump(res, open(os.path.splitext(out_md)[0] + ".json", "w"), indent=1)
+    return res
+
+
+def recorded_prefill_counters():
+    """MFMA busy fraction of the prefill kernel from the committed counter
+    summary, if the prefill source has not changed since it was taken."""
+    if not os.path.exists(PREFILL_COUNTERS):
+        return None
+    rec = json.load(open(PREFILL_COUNTERS))
+    if rec.get("prefill_source_sha256_16") != source_digest(*PREFILL_SRC):
+        return None
+    return rec.get("ratios")
+
+
 def recorded_traffic(workload: str):
     """Traffic per launch from the committed counter summary of this workload,
     if the decode kernel source has not changed since it was taken."""
@@ -551,6 +638,9 @@ def main(argv=None):
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB", "KERNEL_KEY", "OUT_JSON"),
                     help="write the per-launch HBM traffic of a kernel from FETCH_SIZE / "
                          "WRITE_SIZE counter CSVs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="OUT_MD KERNEL_KEY CSV [CSV ...]: write a summary of SQ/GRBM counter "
+                         "CSVs of one kernel (rocprofv3 --pmc passes) and exit")
     ap.add_argument("--commands", nargs="*", default=[],
                     help="the profiler commands recorded in a traffic summary")
     args = ap.parse_args(argv)
@@ -560,6 +650,10 @@ def main(argv=None):
     if args.summarize_traffic:
         f, w, mib, key, out = args.summarize_traffic
         print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands)))
+        return 0
+    if args.summarize_counters:
+        out_md, key, *csvs = args.summarize_counters
+        print(json.dumps(summarize_counters(out_md, key, csvs, args.commands)))
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
