@@ -260,6 +260,7 @@ def prefill_report(steps: int, warmup: int) -> dict:
             "store_ms": round(sto, 4), "store_tokens": c.total_kv_rows,
             "store_GBps": round(sb / (sto * 1e-3) / 1e9, 1),
             "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "store_algorithmic_bytes": sb, "store_traffic_bytes": recorded_store_traffic(),
             "rocprof_counters": recorded_prefill_counters()}
 
 
@@ -455,7 +456,7 @@ def _pmc_per_kernel(counter_csv: str, counter: str):
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key: str,
-                      out_json: str, commands) -> dict:
+                      out_json: str, commands, source: str = DECODE_SRC) -> dict:
     """HBM bytes per launch of the kernel whose name contains kernel_key, from
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the value the
     same counter reads for a plain device copy of copy_mib MiB."""
@@ -497,9 +498,13 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key:
         "fetch_scale": f_scale, "write_scale": w_scale,
         "fetch_bytes": kfv * 1024.0 * f_scale, "write_bytes": kwv * 1024.0 * w_scale,
         "traffic_bytes": kfv * 1024.0 * f_scale + kwv * 1024.0 * w_scale,
-        "decode_source_sha256_16": source_digest(DECODE_SRC),
         "commands": list(commands),
     }
+    if source == DECODE_SRC:
+        res["decode_source_sha256_16"] = source_digest(DECODE_SRC)
+    else:
+        res["source"] = os.path.relpath(source, ROOT)
+        res["source_sha256_16"] = source_digest(source)
     json.dump(res, open(out_json, "w"), indent=1)
     return res
 
@@ -568,6 +573,21 @@ def recorded_prefill_counters():
     if rec.get("prefill_source_sha256_16") != source_digest(*PREFILL_SRC):
         return None
     return rec.get("ratios")
+
+
+STORE_SRC = os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", "store_kv.hip")
+STORE_TRAFFIC = os.path.join(PROFILES, "store_16384_tokens_traffic.json")
+
+
+def recorded_store_traffic():
+    """HBM bytes per launch of the 16,384-token store from the committed
+    counter summary, if the store kernel source has not changed since."""
+    if not os.path.exists(STORE_TRAFFIC):
+        return None
+    rec = json.load(open(STORE_TRAFFIC))
+    if rec.get("source_sha256_16") != source_digest(STORE_SRC):
+        return None
+    return int(round(rec["traffic_bytes"]))
 
 
 def recorded_traffic(workload: str):
@@ -641,6 +661,8 @@ def main(argv=None):
     ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
                     help="OUT_MD KERNEL_KEY CSV [CSV ...]: write a summary of SQ/GRBM counter "
                          "CSVs of one kernel (rocprofv3 --pmc passes) and exit")
+    ap.add_argument("--traffic-source", default=DECODE_SRC,
+                    help="kernel source whose digest a traffic summary records (default: decode)")
     ap.add_argument("--commands", nargs="*", default=[],
                     help="the profiler commands recorded in a traffic summary")
     args = ap.parse_args(argv)
@@ -649,7 +671,8 @@ def main(argv=None):
         return 0
     if args.summarize_traffic:
         f, w, mib, key, out = args.summarize_traffic
-        print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands)))
+        print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands,
+                                           os.path.abspath(args.traffic_source))))
         return 0
     if args.summarize_counters:
         out_md, key, *csvs = args.summarize_counters
@@ -751,6 +774,8 @@ def main(argv=None):
                            "step_ms": round(tc["step_ms"], 4),
                            "step_GBps": round((b + sb) / (tc["step_ms"] * 1e-3) / 1e9, 1),
                            "two_call_step_ms": round(tc["two_call_step_ms"], 4),
+                           "append_algorithmic_bytes": append_bytes(c),
+                           "append_traffic_bytes": recorded_traffic(name),
                            "sum_context_len": int(c.context_lens.sum())}
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(10, args.steps // 5), 3)
