@@ -76,6 +76,45 @@ def copy_probe(mib: int) -> None:
     del src, dst
 
 
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_237_amd", "libpa_probe.so")
+
+
+def read_ceiling(sizes, steps: int = 30) -> dict:
+    """Measured HBM read rate of a load-only kernel shaped like the decode
+    launch (one 8-wave workgroup per CU, each wave streaming contiguous 32 KiB
+    pieces; csrc/read_ceiling.hip), for each byte count in `sizes` (rounded
+    down to 32 KiB): what a launch of that shape and size can stream on this
+    machine, reported beside the vendor peak.  None if the probe library is
+    not built."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_probe_stream_read.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sizes = [int(n) // 32768 * 32768 for n in sizes]
+    buf = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {"kernel": "stream_read_kernel (load-only, decode launch shape)", "workgroups": cus}
+    for n in sizes:
+        def call():
+            st = lib.pa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), n, cus,
+                                          ctypes.c_void_p(sink.data_ptr()),
+                                          ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"pa_probe_stream_read returned {st}")
+        _warm(call, 20)
+        _, ts = _events_ms(call, steps)
+        ms = float(np.median(ts))
+        res[str(n)] = {"us": round(ms * 1e3, 2), "GBps": round(n / (ms * 1e-3) / 1e9, 1)}
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def new_rows(dev):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from device_case import new_rows as _new_rows  # noqa: E402
@@ -703,6 +742,7 @@ def main(argv=None):
     t = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
     copy_probe(args.copy_probe_mib)
     dbytes = decode_bytes(case)
+    ceiling = read_ceiling([append_bytes(case), 4 << 30])
     sbytes = store_bytes(case.batch, case.num_kv_heads)
     abytes = append_bytes(case)
     sum_ctx = int(case.context_lens.sum())
@@ -730,6 +770,7 @@ def main(argv=None):
                    "max_context_len": case.max_context_len, "num_blocks": case.num_blocks,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "hbm_read_ceiling_measured": ceiling,
         "attended_tokens_per_s": round(sum_ctx / (ms_step * 1e-3), 1),
         "step_launch": "one pa_decode_append launch per step (store of the new tokens + decode), "
                        "launched back to back on one stream",

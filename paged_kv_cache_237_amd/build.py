@@ -16,9 +16,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+# measurement helper for the benchmark (a load-only streaming kernel), kept
+# out of libpa so that the library exports only the pa_* interface
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 
 SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "prefill.hip", "blocks.hip",
            "block_manager.cpp", "checks.hip"]
+PROBE_SOURCES = ["read_ceiling.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5",
@@ -40,11 +44,18 @@ def torch_lib_dir() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so; returns its path."""
+    """Compile every source and link libpa.so (and the benchmark's probe
+    library libpa_probe.so); returns the path of libpa.so."""
+    _build_lib(SOURCES, LIB, verbose)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _build_lib(sources, lib_path: str, verbose: bool) -> None:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     procs, objs = [], []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
@@ -67,14 +78,13 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
     tl = torch_lib_dir()
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     link = ["g++", "-shared", "-o", tmp, *objs, f"-L{tl}", "-l:libamdhip64.so",
             f"-Wl,-rpath,{tl}", "-Wl,--disable-new-dtags", "-Wl,--no-undefined"]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
 
 
 if __name__ == "__main__":

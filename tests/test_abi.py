@@ -29,6 +29,19 @@ def test_header_declares_the_expected_entry_points():
 
 
 @needs_lib
+def test_library_exports_only_the_declared_interface():
+    """libpa exports the pa_* interface and nothing of the benchmark's probe,
+    which lives in its own library."""
+    nm = os.popen(f"nm -D --defined-only {pa.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (pa_[a-z_0-9]+)$", nm, flags=re.M))
+    assert exported == set(declared_functions())
+    probe = os.path.join(os.path.dirname(pa.LIB_PATH), "libpa_probe.so")
+    if os.path.exists(probe):
+        pnm = os.popen(f"nm -D --defined-only {probe}").read()
+        assert set(re.findall(r"\bT (pa_[a-z_0-9]+)$", pnm, flags=re.M)) == {"pa_probe_stream_read"}
+
+
+@needs_lib
 def test_library_exports_every_declared_symbol():
     lib = pa.lib()
     for name in declared_functions():
