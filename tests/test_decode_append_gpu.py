@@ -60,6 +60,46 @@ def test_qwen3_0_6b_decode_full():
     check_append(wl.qwen3_0_6b_decode())
 
 
+def check_append_sampled(case, seqs):
+    """A full-size call (the launch the benchmark times); outputs of the
+    sampled sequences against the oracle, and their cache rows -- the new
+    token's included -- against the oracle's store."""
+    print(f"[decode_append] {case.name} sampled seqs={list(seqs)}", flush=True)
+    dev = place(case)
+    k_new, v_new = new_rows(dev)
+    out = bf16_out_to_f64(run_append(dev, k_new, v_new))
+    kp, vp = oracle_pools(case, seqs, poison=False)
+    q = wl.bits_to_numpy(case.q_all())
+    for b in seqs:
+        n = int(case.context_lens[b])
+        for i in range(wl.blocks_for(n)):
+            blk = int(case.block_table[b, i])
+            rows = min(wl.BLOCK_SIZE, n - i * wl.BLOCK_SIZE)
+            kd = wl.bits_to_numpy(dev.k_cache[blk].view(torch.int16))
+            vd = wl.bits_to_numpy(dev.v_cache[blk].view(torch.int16))
+            assert np.array_equal(kd[:, :, :rows], kp[blk][:, :, :rows]), (b, i)
+            assert np.array_equal(vd[:, :rows], vp[blk][:, :rows]), (b, i)
+    got = np.stack([out[b] for b in seqs])
+    ref = np.stack([oracle.decode_seq(q[b], kp, vp, case.block_table[b], int(case.context_lens[b]),
+                                      case.scale) for b in seqs])
+    return compare(got, ref, case.name)
+
+
+def test_qwen3_4b_decode_sampled():
+    # 256 sequences, lognormal lengths up to 32,768: shortest, longest and a
+    # seeded sample
+    case = wl.qwen3_4b_decode()
+    order = np.argsort(case.context_lens)
+    seqs = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]),
+                   *np.random.default_rng(4).choice(case.batch, 10, replace=False).tolist()})
+    check_append_sampled(case, seqs)
+
+
+def test_long_context_decode_sampled():
+    # 8 x 131,072 tokens: every segment is cut across many waves
+    check_append_sampled(wl.long_context_decode(), [2, 7])
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (4, 1)])
 def test_edge_lengths_all_group_sizes(hq, hkv):
     check_append(wl.make_case(f"append_edge_{hq}_{hkv}", "decode", 300 + hq + hkv, EDGE, hq, hkv))
