@@ -493,8 +493,15 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
       }
     }
     const bool next_ok = has_next && nb < a.batch;
-    // the appended token of a segment this wave finishes whole: its rows are
-    // loaded under the segment's last tile
+    // the appended token of a segment this wave streams whole: its rows (and
+    // its slot) are loaded under the segment's last tile, for the fold at the
+    // end of the piece
+    NewToken tk_next;
+    tk_next.ok = false;
+    if constexpr (Append) {
+      if (seg_end && piece_t0 == 0) tk_next = new_token_load(a, b, g);
+    }
+    // the next segment's q, loaded under this segment's last tile
     uint4 qn[kQPerLane];
     if (seg_end && next_ok) {
       if constexpr (!Causal) {
@@ -622,7 +629,8 @@ __device__ int stream_run(const DecodeArgs& a, const TileScan& sc, int pos, int 
         if constexpr (Append) {
           // lane holds dims 8*(lane & 15) .. +7 of every head; q is still
           // this segment's in LDS
-          const NewToken tk = new_token(a, b, g);
+          const NewToken tk = tk_next;
+          new_token_store(a, tk, g);
           if (tk.ok) {
             float vn[8];
             unpack8(tk.vc, vn);
