@@ -470,11 +470,13 @@ def summarize_stats(stats_csv: str, out_md: str, command: str) -> None:
     rows = _read_csv(stats_csv)
     lines = ["# rocprofv3 kernel statistics", "", "Command (run from the repository root):", "",
              "```", command, "```", "",
-             "Library kernels and device copies only; the other kernels of the run are torch "
-             "kernels that generate the seeded inputs before timing.", "",
+             "Library kernels, the benchmark's load-only read-ceiling kernel and device copies "
+             "only; the other kernels of the run are torch kernels that generate the seeded "
+             "inputs before timing.", "",
              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
-        if "pa::" not in r["Name"] and "copyBuffer" not in r["Name"]:
+        if ("pa::" not in r["Name"] and "copyBuffer" not in r["Name"]
+                and "stream_read_kernel" not in r["Name"]):
             continue
         name = r["Name"]
         short = name if len(name) < 70 else name[:67] + "..."
