@@ -148,12 +148,14 @@ size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_
  *                   (must be <= max_blocks_per_seq*block_size).
  *   scale         : the logit scale (e.g. 1/sqrt(head_dim)); finite.
  *   workspace     : >= pa_decode_workspace_size(...) bytes of device memory,
- *                   256-B aligned.  It holds one arrival counter per
- *                   (sequence, kv head), which must be zero before the first
- *                   call (zero-fill the whole workspace once) and which every
- *                   call resets to zero, plus partial results that are scratch
- *                   and need no clearing.  Calls that overlap in time must not
- *                   share a workspace.
+ *                   256-B aligned.  It holds partial results from its start
+ *                   (scratch, no clearing needed) and one arrival counter per
+ *                   (sequence, kv head) at its end, which must be zero before
+ *                   the first call (zero-fill the whole workspace once) and
+ *                   which every call resets to zero.  A workspace sized for
+ *                   the largest call of a series (batch, heads) serves every
+ *                   call of the series, in any order.  Calls that overlap in
+ *                   time must not share a workspace.
  *   Source: CSDN essay, first and third sections; vLLM decode kernel
  *   description in the same essay.
  */

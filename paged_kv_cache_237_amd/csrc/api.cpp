@@ -119,8 +119,14 @@ int64_t decode_waves(int cus, int32_t batch, int32_t num_kv_heads, int32_t max_c
   return std::max<int64_t>(1, std::min(w, tiles_upper));
 }
 
-// Workspace: one int arrival counter per (sequence, kv head) segment, padded
-// to 256 bytes, then the partial records (batch*Hkv + waves of them).
+// Workspace: the partial records (batch*Hkv + waves of them) from its start,
+// one int arrival counter per (sequence, kv head) segment at its end (the
+// last 256-byte-aligned counter region that fits).  Records never reach the
+// counters of a later call that the same workspace covers: a call's records
+// end where a workspace sized for the largest call's records and counters
+// leaves room for its counters, whatever the batch of the calls before it
+// (with the counters first, a call with a small batch would write records
+// over counter slots that a later, larger batch expects to be zero).
 size_t decode_counter_bytes(int32_t batch, int32_t num_kv_heads) {
   const size_t bytes = size_t(int64_t(batch) * num_kv_heads) * sizeof(int);
   return (bytes + 255) & ~size_t(255);
@@ -235,9 +241,10 @@ int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, 
     a.block_table = block_table;
     a.ctx_lens = context_lens;
     a.out = static_cast<uint16_t*>(out);
-    a.counters = static_cast<int*>(workspace);
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    decode_counter_bytes(batch, num_kv_heads));
+    a.ws = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<int*>(
+        static_cast<char*>(workspace) +
+        ((workspace_bytes - decode_counter_bytes(batch, num_kv_heads)) & ~size_t(255)));
     a.num_blocks = num_blocks;
     a.batch = batch;
     a.hkv = num_kv_heads;

@@ -137,6 +137,40 @@ def test_repeated_calls_are_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_workspace_reused_across_batch_sizes():
+    """One workspace sized for the largest batch, used by calls of different
+    batch sizes in turn -- 64 sequences, then 8 long ones (every segment cut,
+    partial records all over the workspace), then 64 again, then 8 again:
+    each call gives the same bits as the same call on a fresh workspace (its
+    arrival counters must still be zero, whatever the calls before it wrote
+    into the workspace)."""
+    big = wl.qwen3_0_6b_decode()
+    small = wl.make_case("ws_reuse_small", "decode", 40,
+                         [20000, 30000, 9000, 15000, 25000, 12000, 31000, 8000], 16, 8)
+    devs = {"big": place(big), "small": place(small)}
+
+    def call(dev, ws):
+        c = dev.case
+        out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        pa.decode(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens,
+                  c.max_context_len, c.scale, ws)
+        torch.cuda.synchronize()
+        return out.view(torch.int16).clone()
+
+    fresh = {k: call(d, pa.alloc_decode_workspace(d.case.batch, 16, 8)) for k, d in devs.items()}
+    shared = pa.alloc_decode_workspace(big.batch, 16, 8)
+    for i, k in enumerate(["big", "small", "big", "small", "big"]):
+        got = call(devs[k], shared)
+        assert torch.equal(got, fresh[k]), f"call {i} ({k}) differs from a fresh workspace"
+    # and the results are right
+    kp, vp = oracle_pools(small)
+    ref = oracle.decode(wl.bits_to_numpy(small.q_all()), kp, vp, small.block_table,
+                        small.context_lens, small.scale)
+    compare(bf16_out_to_f64(fresh["small"].view(torch.bfloat16)), ref, small.name)
+
+
 def test_empty_batch_is_a_no_op():
     k, v = pa.alloc_cache(2, 8, "cuda")
     q = torch.empty((0, 16, 128), dtype=torch.bfloat16, device="cuda")
