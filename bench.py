@@ -79,7 +79,7 @@ def copy_probe(mib: int) -> None:
 PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_237_amd", "libpa_probe.so")
 
 
-def read_ceiling(sizes, steps: int = 30) -> dict:
+def read_ceiling(sizes, labels, steps: int = 30) -> dict:
     """Measured HBM read rate of a load-only kernel shaped like the decode
     launch (one 8-wave workgroup per CU, each wave streaming contiguous 32 KiB
     pieces; csrc/read_ceiling.hip), for each byte count in `sizes` (rounded
@@ -99,7 +99,7 @@ def read_ceiling(sizes, steps: int = 30) -> dict:
     sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     res = {"kernel": "stream_read_kernel (load-only, decode launch shape)", "workgroups": cus}
-    for n in sizes:
+    for n, label in zip(sizes, labels):
         def call():
             st = lib.pa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), n, cus,
                                           ctypes.c_void_p(sink.data_ptr()),
@@ -109,7 +109,7 @@ def read_ceiling(sizes, steps: int = 30) -> dict:
         _warm(call, 20)
         _, ts = _events_ms(call, steps)
         ms = float(np.median(ts))
-        res[str(n)] = {"us": round(ms * 1e3, 2), "GBps": round(n / (ms * 1e-3) / 1e9, 1)}
+        res[label] = {"bytes": n, "us": round(ms * 1e3, 2), "GBps": round(n / (ms * 1e-3) / 1e9, 1)}
     del buf, sink
     torch.cuda.empty_cache()
     return res
@@ -744,7 +744,7 @@ def main(argv=None):
     t = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
     copy_probe(args.copy_probe_mib)
     dbytes = decode_bytes(case)
-    ceiling = read_ceiling([append_bytes(case), 4 << 30])
+    ceiling = read_ceiling([append_bytes(case), 4 << 30], ["step_bytes", "4GiB"])
     sbytes = store_bytes(case.batch, case.num_kv_heads)
     abytes = append_bytes(case)
     sum_ctx = int(case.context_lens.sum())
@@ -753,6 +753,11 @@ def main(argv=None):
     app_gbs = abytes / (t["append_ms"] * 1e-3) / 1e9
     dec_gbs = dbytes / (t["decode_ms"] * 1e-3) / 1e9
     flushed = t["decode_ms_flushed"]
+    if ceiling is not None:
+        # the step's own rate against what a load-only launch of its shape
+        # and size streams on this machine
+        ceiling["step_frac_of_step_bytes_ceiling"] = round(
+            step_gbs / ceiling["step_bytes"]["GBps"], 4)
     line = {
         "metric": METRIC,
         "value": round(step_gbs, 1),
