@@ -9,8 +9,8 @@ physical blocks shuffled, pool +10 %).  Inputs are seeded synthetic data
 placed in HBM before timing.  Other workloads are reported under "extra"
 (they are parity-test shapes; the headline line is the one above).
 
-Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one
-GPU only.
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: the library and its
+benchmark run on one GPU.
 """
 
 from __future__ import annotations
