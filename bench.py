@@ -550,9 +550,11 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key:
     return res
 
 
-# the prefill kernel and the device headers it includes
-PREFILL_SRC = tuple(os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", f)
-                    for f in ("prefill.hip", "pa_device.hpp", "pa_internal.hpp"))
+# the prefill kernel, the device headers it includes and the build script
+# that holds its compiler options
+PREFILL_SRC = tuple(os.path.join(ROOT, "paged_kv_cache_237_amd", *f)
+                    for f in (("csrc", "prefill.hip"), ("csrc", "pa_device.hpp"),
+                              ("csrc", "pa_internal.hpp"), ("build.py",)))
 PREFILL_COUNTERS = os.path.join(PROFILES, "prefill_8x2048_sq_counters.json")
 
 

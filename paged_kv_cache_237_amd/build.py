@@ -24,6 +24,13 @@ SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "prefill.hip", "blocks.hip",
            "block_manager.cpp", "checks.hip"]
 PROBE_SOURCES = ["read_ceiling.hip"]
 
+# Per-source compiler options.  The prefill kernel is scheduled with LLVM's
+# ILP-first AMDGPU scheduler instead of the default occupancy-first one: same
+# registers, bit-identical results, and its MFMA / softmax interleave runs
+# 1-3 % faster on every prefill workload measured (8 x 2048 causal, chunked
+# prefill mixed with decode rows, multi-query decode through pa_prefill).
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-mcode-object-version=5",
     # no packed-fp32 instructions in generated code
@@ -59,8 +66,8 @@ def _build_lib(sources, lib_path: str, verbose: bool) -> None:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
-               os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, *lang,
+               "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
