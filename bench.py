@@ -812,6 +812,7 @@ def main(argv=None):
             c = wl.CONFIGS[name]()
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             tc = time_decode(c, max(10, args.steps // 5), 3)
+            cl = read_ceiling([append_bytes(c)], ["step_bytes"])
             b, d = decode_bytes(c), tc["decode_ms"]
             sb = store_bytes(c.batch, c.num_kv_heads)
             extra[name] = {"decode_ms": round(d, 4), "decode_GBps": round(b / (d * 1e-3) / 1e9, 1),
@@ -825,6 +826,9 @@ def main(argv=None):
                            "step_GBps": round((b + sb) / (tc["step_ms"] * 1e-3) / 1e9, 1),
                            "two_call_step_ms": round(tc["two_call_step_ms"], 4),
                            "append_algorithmic_bytes": append_bytes(c),
+                           "read_ceiling_same_bytes_us": cl["step_bytes"]["us"] if cl else None,
+                           "append_frac_of_same_size_ceiling": (
+                               round(cl["step_bytes"]["us"] / (tc["append_ms"] * 1e3), 4) if cl else None),
                            "append_traffic_bytes": recorded_traffic(name),
                            "sum_context_len": int(c.context_lens.sum())}
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
