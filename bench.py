@@ -300,7 +300,19 @@ def prefill_report(steps: int, warmup: int) -> dict:
             "store_GBps": round(sb / (sto * 1e-3) / 1e9, 1),
             "store_frac_of_hbm_peak": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "store_algorithmic_bytes": sb, "store_traffic_bytes": recorded_store_traffic(),
-            "rocprof_counters": recorded_prefill_counters()}
+            "rocprof_counters": recorded_prefill_counters(),
+            # the same schema as the headline's roofline, for the prefill and
+            # store kernels of this workload
+            "prefill_roofline": {"bound": "mfma", "kernel": "prefill_kernel<2>",
+                                 "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                 "traffic": None, "algorithmic_flops_per_launch": fl},
+            "store_roofline": {"bound": "hbm", "kernel": "store_kv_kernel",
+                               "achieved": round(sb / (sto * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s",
+                               "frac": round(sb / (sto * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "traffic": recorded_store_traffic(),
+                               "algorithmic_bytes_per_launch": sb}}
 
 
 def varlen_report(name: str, steps: int, warmup: int) -> dict:
