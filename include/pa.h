@@ -154,7 +154,9 @@ size_t pa_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_
  *                   the first call (zero-fill the whole workspace once) and
  *                   which every call resets to zero.  A workspace sized for
  *                   the largest call of a series (batch, heads) serves every
- *                   call of the series, in any order.  Calls that overlap in
+ *                   call of the series, in any order, when every call passes
+ *                   the same workspace_bytes (the allocation's size: the
+ *                   counters' place is taken from it).  Calls that overlap in
  *                   time must not share a workspace.
  *   Source: CSDN essay, first and third sections; vLLM decode kernel
  *   description in the same essay.
