@@ -255,8 +255,13 @@ def prefill_flops(case: wl.PagedCase) -> int:
     return 4 * case.head_dim * case.num_q_heads * pairs
 
 
+PREFILL_SPREAD = {}
+
+
 def time_prefill(case: wl.PagedCase, steps: int, warmup: int):
-    """Times store (all prompt tokens) + prefill; returns (store_ms, prefill_ms)."""
+    """Times store (all prompt tokens) + prefill, `steps` calls after the
+    warm-up; returns the medians (store_ms, prefill_ms) and records the
+    prefill min / max in PREFILL_SPREAD."""
     dev = place(case)
     out = torch.empty((case.total_q_rows, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
                       device="cuda")
@@ -281,8 +286,12 @@ def time_prefill(case: wl.PagedCase, steps: int, warmup: int):
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    sto = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    pre = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # medians of the per-call times (min and max in PREFILL_SPREAD)
+    sts = [e[0].elapsed_time(e[1]) for e in evs]
+    pts = [e[1].elapsed_time(e[2]) for e in evs]
+    sto, pre = float(np.median(sts)), float(np.median(pts))
+    PREFILL_SPREAD[case.name] = {"prefill_ms_min": round(min(pts), 4), "prefill_ms_max": round(max(pts), 4),
+                                 "reps": len(pts)}
     del dev
     torch.cuda.empty_cache()
     return sto, pre
@@ -294,7 +303,8 @@ def prefill_report(steps: int, warmup: int) -> dict:
     fl = prefill_flops(c)
     sb = store_bytes(c.total_kv_rows, c.num_kv_heads)
     tf = fl / (pre * 1e-3) / 1e12
-    return {"workload": c.name, "prefill_ms": round(pre, 4), "causal_gflop": round(fl / 1e9, 3),
+    return {"workload": c.name, "prefill_ms": round(pre, 4), **PREFILL_SPREAD.get(c.name, {}),
+            "causal_gflop": round(fl / 1e9, 3),
             "prefill_TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
             "store_ms": round(sto, 4), "store_tokens": c.total_kv_rows,
             "store_GBps": round(sb / (sto * 1e-3) / 1e9, 1),
@@ -326,7 +336,8 @@ def varlen_report(name: str, steps: int, warmup: int) -> dict:
     kvb = int(c.context_lens.sum()) * c.num_kv_heads * c.head_dim * 2 * 2
     tf = fl / (pre * 1e-3) / 1e12
     gbs = kvb / (pre * 1e-3) / 1e9
-    return {"workload": c.name, "prefill_ms": round(pre, 4), "query_rows": c.total_q_rows,
+    return {"workload": c.name, "prefill_ms": round(pre, 4), **PREFILL_SPREAD.get(c.name, {}),
+            "query_rows": c.total_q_rows,
             "sum_context_len": int(c.context_lens.sum()), "causal_gflop": round(fl / 1e9, 3),
             "TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
             "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -844,10 +855,10 @@ def main(argv=None):
                            "append_traffic_bytes": recorded_traffic(name),
                            "sum_context_len": int(c.context_lens.sum())}
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
-        extra["prefill_8x2048"] = prefill_report(max(10, args.steps // 5), 3)
+        extra["prefill_8x2048"] = prefill_report(max(30, args.steps // 5), 3)
         for name in ("chunked_prefill_mixed", "multi_query_decode", "long_prefix_chunk"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
-            extra[name] = varlen_report(name, max(10, args.steps // 5), 3)
+            extra[name] = varlen_report(name, max(30, args.steps // 5), 3)
         print("[bench] extra multi-query decode (pa_decode_multi)", file=sys.stderr, flush=True)
         extra["multi_query_decode_multi"] = decode_multi_report(max(10, args.steps // 5), 3)
         print("[bench] extra block copy / swap", file=sys.stderr, flush=True)
