@@ -143,8 +143,12 @@ size_t decode_ws_bytes(int32_t batch, int32_t num_kv_heads, int group, int64_t w
 // 256-CU gfx950 part is assumed, so that the workspace size does not depend
 // on which device is current -- the split only affects speed) can leave CUs
 // idle while a few blocks stream long contexts; only then are blocks split,
-// into enough parts for about four workgroups per slot (every other launch
-// gets max_splits = 1: no records, no merge, no empty workgroups).
+// into as many parts as fill every slot once: floor(slots / blocks), at most
+// kPrefillMaxSplits (every other launch gets max_splits = 1: no records, no
+// merge, no empty workgroups).  One workgroup per slot beat several: with
+// ~4 per slot the extra parts added merge traffic and prologues, and a
+// count that is not a multiple of the slots leaves some slots a second
+// workgroup while the rest idle.
 struct PrefillSplit {
   int split_tiles, max_splits, nqb_max;
   size_t ml_bytes, o_bytes;
@@ -163,7 +167,7 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
   ps.nqb_max = (max_seqlen_q + qb - 1) / qb;
   const int64_t slots = kPrefillSlots;
   const int64_t blocks = std::max<int64_t>(1, int64_t(batch) * num_kv_heads * ps.nqb_max);
-  const int64_t want = blocks >= slots ? 1 : (4 * slots + blocks - 1) / blocks;
+  const int64_t want = blocks >= slots ? 1 : slots / blocks;
   ps.max_splits = int(std::max<int64_t>(
       1, std::min<int64_t>(want, (max_tiles + ps.split_tiles - 1) / ps.split_tiles)));
   if (ps.max_splits == 1) {
