@@ -239,7 +239,7 @@ int pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v
 /*
  * pa_prefill_workspace_size -- bytes of device workspace pa_prefill needs for
  * these sizes (0 when no query block can be split: contexts of at most
- * 2048 tokens, i.e. max_blocks_per_seq <= 8).  Also 0 for invalid arguments;
+ * 1024 tokens, i.e. max_blocks_per_seq <= 4).  Also 0 for invalid arguments;
  * pa_prefill then reports the error.
  */
 size_t pa_prefill_workspace_size(int32_t batch, int64_t total_q_rows, int32_t max_seqlen_q,

@@ -94,7 +94,7 @@ struct PrefillArgs {
 
 // Query rows per prefill workgroup, key tiles per split part, parts per block.
 constexpr int kPrefillRows = 128;
-constexpr int kPrefillSplitTiles = 32;
+constexpr int kPrefillSplitTiles = 16;
 constexpr int kPrefillMaxSplits = 16;
 
 struct CopyBlocksArgs {

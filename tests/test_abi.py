@@ -201,10 +201,11 @@ def test_prefill_rejects_bad_arguments_on_the_host():
     assert call(scale=float("inf")) == -2
     assert call(tq=-1) == -2
     assert call(tq=0) == 0
-    # contexts of up to 2048 tokens (8 blocks) are never split: no workspace
+    # contexts of up to 1024 tokens (4 blocks) are never split: no workspace
     # (not called here: with valid arguments the call would launch on the
     # fake pointers)
-    assert lib.pa_prefill_workspace_size(2, 150, 100, 16, 8, 128, 256, 8) == 0
+    assert lib.pa_prefill_workspace_size(2, 150, 100, 16, 8, 128, 256, 4) == 0
+    assert lib.pa_prefill_workspace_size(2, 150, 100, 16, 8, 128, 256, 8) > 0
     # longer ones may be: the workspace is then required, aligned and large enough
     need = lib.pa_prefill_workspace_size(2, 150, 100, 16, 8, 128, 256, 40)
     assert need > 0
