@@ -97,6 +97,16 @@ def test_prefill_long_prefix_split_many_ways(hq, hkv):
     check(case, seqs_full={1, 2, 3}, heads_sampled=[0, hq - 1])
 
 
+def test_prefill_split_between_half_and_all_slots():
+    """A 2,160-token chunk over an 8,192-token prefix: 270 query blocks, more
+    than half the workgroup slots, so each block's keys are cut into several
+    parts that run in a few rounds, merged through the workspace."""
+    case = wl.make_case("chunk_270_blocks", "prefill", 46, [8192 + 2160], 16, 8, q_lens=[2160])
+    assert pa.prefill_workspace_size(case.batch, case.total_q_rows, case.max_q_len, 16, 8,
+                                     case.max_blocks_per_seq) > 0
+    check(case, seqs_full=set(), heads_sampled=[0, 7, 15])
+
+
 def test_long_prefix_chunk():
     """A 512-token chunk over a 65,536-token cached prefix: 64 query blocks
     for 256 CUs, so each block's context is split across workgroups."""
