@@ -2,12 +2,13 @@
 
 One step = the whole path over one batch: each sequence's new token is
 stored into its slot and attended together with its full paged context, as
-one pa_decode_append launch (pa_store_kv + pa_decode is timed beside it).  The default
-workload is the Qwen3-0.6B-shaped decode layer (batch 64, context lengths
-uniform on 512..4096, 16 query / 8 kv heads, head dim 128, 256-token blocks,
-physical blocks shuffled, pool +10 %).  Inputs are seeded synthetic data
-placed in HBM before timing.  Other workloads are reported under "extra"
-(they are parity-test shapes; the headline line is the one above).
+one pa_decode_append launch (pa_store_kv + pa_decode is timed beside it).  The
+default workload is the largest decode configuration that fits one GPU:
+8 sequences of 131,072 cached tokens each (512 blocks per sequence), 32 query
+/ 8 kv heads, head dim 128, 256-token blocks, physical blocks shuffled, pool
++10 %: 4.29 GB of K/V read per step.  Inputs are seeded synthetic data placed
+in HBM before timing.  The other decode shapes, the prefill and the next-step
+workloads are reported under "extra", each with its own roofline object.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: the library and its
 benchmark run on one GPU.
@@ -573,12 +574,20 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key:
     return res
 
 
-# the prefill kernel, the device headers it includes and the build script
-# that holds its compiler options
-PREFILL_SRC = tuple(os.path.join(ROOT, "paged_kv_cache_237_amd", *f)
-                    for f in (("csrc", "prefill.hip"), ("csrc", "pa_device.hpp"),
-                              ("csrc", "pa_internal.hpp"), ("build.py",)))
+# the prefill kernel and the headers it includes; its compiler options are
+# added to the digest from the build script's option lists (prefill_digest)
+PREFILL_SRC = tuple(os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", f)
+                    for f in ("prefill.hip", "pa_device.hpp", "pa_common.hpp", "pa_prefill.hpp"))
 PREFILL_COUNTERS = os.path.join(PROFILES, "prefill_8x2048_sq_counters.json")
+
+
+def prefill_digest() -> str:
+    """Digest of what the prefill kernel's code depends on: its source, the
+    headers it includes and the hipcc options it is compiled with."""
+    import hashlib
+    from paged_kv_cache_237_amd import build as b
+    flags = json.dumps([b.HIPCC_FLAGS, b.SOURCE_FLAGS.get("prefill.hip", [])]).encode()
+    return hashlib.sha256(source_digest(*PREFILL_SRC).encode() + flags).hexdigest()[:16]
 
 
 def summarize_counters(out_md: str, kernel_key: str, csvs, commands) -> dict:
@@ -617,7 +626,7 @@ def summarize_counters(out_md: str, kernel_key: str, csvs, commands) -> dict:
             ratios["wait_inst_lds_frac_of_wave_cycles"] = d["SQ_WAIT_INST_LDS"][0] / d["SQ_WAVE_CYCLES"][0]
     res = {"kernel_key": kernel_key, "counters": {k: v for k, (v, _) in sorted(merged.items())},
            "dispatches": min(n for _, n in merged.values()), "ratios": ratios,
-           "prefill_source_sha256_16": source_digest(*PREFILL_SRC), "commands": list(commands)}
+           "prefill_source_sha256_16": prefill_digest(), "commands": list(commands)}
     lines = [f"# `{kernel_key}` SQ counters", "",
              "Commands (run from the repository root, one pass each; values are summed over the "
              "hardware instances and averaged over the kernel's dispatches):", "", "```",
@@ -636,7 +645,7 @@ def recorded_prefill_counters():
     if not os.path.exists(PREFILL_COUNTERS):
         return None
     rec = json.load(open(PREFILL_COUNTERS))
-    if rec.get("prefill_source_sha256_16") != source_digest(*PREFILL_SRC):
+    if rec.get("prefill_source_sha256_16") != prefill_digest():
         return None
     return rec.get("ratios")
 
@@ -668,12 +677,18 @@ def recorded_traffic(workload: str):
     return int(round(rec["traffic_bytes"]))
 
 
-def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
-    """The oracle as it stands, timed on the host cores on a bounded sample of
-    the same workload: whole sequences in batch order (wrapping around to the
-    first sequence again) until about budget_s of oracle time."""
-    import oracle
+def _oracle_threads() -> int:
     from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+
+
+def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0, max_seqs: int = 0) -> dict:
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload: whole sequences in batch order until about budget_s of
+    oracle time; with max_seqs > 0 only the first max_seqs sequences are built
+    and the sample cycles over them (a 131,072-token sequence takes ~3 s of
+    oracle time but ~12 s to build its host pools, which are not timed)."""
+    import oracle
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from paged_harness import oracle_pools  # noqa: E402
@@ -681,8 +696,9 @@ def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
     q = wl.bits_to_numpy(case.q_all())
     pools = {}
     done_ctx, done_seqs, spent = 0, 0, 0.0
+    cycle = case.batch if max_seqs <= 0 else min(max_seqs, case.batch)
     while spent < budget_s:
-        b = done_seqs % case.batch
+        b = done_seqs % cycle
         if b not in pools:
             pools[b] = oracle_pools(case, [b], poison=False)
         kp, vp = pools[b]
@@ -693,14 +709,165 @@ def cpu_baseline(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
         done_seqs += 1
         if len(pools) > 8:
             pools.pop(next(iter(pools)))
+    del pools
     bytes_done = done_ctx * case.num_kv_heads * case.head_dim * 2 * 2
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(bytes_done / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    which = "in batch order" if cycle == case.batch else f"cycling over the first {cycle}"
+    return {"value": round(bytes_done / spent / 1e9, 4), "unit": "GB/s", "cores": _oracle_threads(),
             "kind": "oracle",
-            "sample": f"{case.name}: float64 oracle decode of {done_seqs} whole sequences in "
-                      f"batch order ({done_ctx} attended tokens x {case.num_q_heads} q heads, "
+            "sample": f"{case.name}: float64 oracle decode of {done_seqs} whole sequences {which} "
+                      f"({done_ctx} attended tokens x {case.num_q_heads} q heads, "
                       f"{spent:.1f} s of oracle time; {done_ctx / spent:.0f} attended tokens/s); "
                       f"GB/s counts the same algorithmic K/V bytes as the GPU figure"}
+
+
+def cpu_baseline_prefill(case: wl.PagedCase, budget_s: float = 10.0) -> dict:
+    """The oracle's causal prefill timed on the host cores: whole sequences in
+    batch order until about budget_s of oracle time, reported in causal
+    TFLOP/s (the same FLOP count as the GPU figure)."""
+    import oracle
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from paged_harness import oracle_pools  # noqa: E402
+
+    q = wl.bits_to_numpy(case.q_all())
+    flops, seqs, spent = 0, 0, 0.0
+    pools = None
+    while spent < budget_s and seqs < 4 * case.batch:
+        b = seqs % case.batch
+        if pools is None:
+            pools = oracle_pools(case, poison=False)
+        kp, vp = pools
+        lo, hi = int(case.q_offsets[b]), int(case.q_offsets[b + 1])
+        t0 = time.perf_counter()
+        oracle.prefill_seq(q[lo:hi], kp, vp, case.block_table[b], int(case.context_lens[b]), case.scale)
+        spent += time.perf_counter() - t0
+        ql, n = hi - lo, int(case.context_lens[b])
+        flops += 4 * case.head_dim * case.num_q_heads * (ql * (n - ql + 1) + ql * (ql - 1) // 2)
+        seqs += 1
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": f"{case.name}: float64 oracle causal prefill of {seqs} whole sequences in batch "
+                      f"order ({flops / 1e9:.1f} causal GFLOP, {spent:.1f} s of oracle time)"}
+
+
+def versions() -> dict:
+    """Software and device the figures were measured with."""
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    p = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "torch_hip": torch.version.hip, "rocm": rocm,
+            "device": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "python": sys.version.split()[0]}
+
+
+def decode_split_plan(case: wl.PagedCase, cus: int, append: bool = True) -> dict:
+    """How a decode launch of this workload cuts its work (the rule the
+    library applies on the host and in the kernel's prologue): every
+    (sequence, kv head) is a segment of ceil(n / 64) tiles of 64 tokens (n =
+    the context, minus the appended token for pa_decode_append), the segments
+    are laid end to end and cut into one run per wave, runs weighted 12 on
+    even- and 11 on odd-numbered XCDs (equal runs when there are too few
+    tiles); a segment whose first and last tiles fall in different runs is
+    merged from partial states."""
+    g = case.num_q_heads // case.num_kv_heads
+    nw = 4 if g == 8 else 8
+    cap = case.max_blocks_per_seq * case.block_size
+    ctx = np.clip(case.context_lens.astype(np.int64), 0, cap)
+    streamed = np.where(ctx > 0, ctx - 1, 0) if append else ctx
+    nt = (streamed + 63) // 64
+    hkv = case.num_kv_heads
+    total = int(nt.sum()) * hkv
+    tiles_upper = case.batch * hkv * ((case.max_context_len + 63) // 64)
+    n_waves = max(1, min(cus * nw, tiles_upper))
+    we, wo = 12, 11
+
+    def weight_before(w):
+        blk, wv = w // nw, w % nw
+        s0 = (blk >> 1) * nw * (we + wo)
+        return s0 + nw * we + wv * wo if blk & 1 else s0 + wv * we
+
+    ssum = weight_before(n_waves)
+    weighted = total * min(we, wo) >= ssum
+    per = 0 if weighted else -(-total // n_waves)
+
+    def run_start(w):
+        if per:
+            return min(w * per, total)
+        return total if w >= n_waves else total * weight_before(w) // ssum
+
+    starts = np.array([run_start(w) for w in range(n_waves + 1)], dtype=np.int64)
+    seg_nt = np.repeat(nt, hkv)
+    seg_lo = np.concatenate([[0], np.cumsum(seg_nt)[:-1]])
+    live = seg_nt > 0
+    w_first = np.searchsorted(starts, seg_lo[live], side="right") - 1
+    w_last = np.searchsorted(starts, seg_lo[live] + seg_nt[live] - 1, side="right") - 1
+    lens = np.diff(starts)
+    return {"waves": int(n_waves), "workgroups": int(-(-n_waves // nw)), "waves_per_workgroup": nw,
+            "total_tiles": total, "tile_tokens": 64,
+            "runs": "weighted 12:11 (even:odd XCD)" if weighted else f"equal, {per} tiles",
+            "tiles_per_wave_min_max": [int(lens.min()), int(lens.max())],
+            "segments": int(live.sum()), "segments_merged": int((w_first != w_last).sum())}
+
+
+def decode_entry(case: wl.PagedCase, t: dict, cus: int, ceiling=None) -> dict:
+    """Figures of one decode workload from time_decode's timings: the step
+    rate, the step kernel's roofline (pa_decode_append: HIP events around
+    single launches on the stream the kernel runs on), plain pa_decode's,
+    and the split plan."""
+    g = case.num_q_heads // case.num_kv_heads
+    dbytes, abytes = decode_bytes(case), append_bytes(case)
+    sbytes = store_bytes(int((case.context_lens > 0).sum()), case.num_kv_heads)
+    sum_ctx = int(case.context_lens.sum())
+    step_gbs = (dbytes + sbytes) / (t["step_ms"] * 1e-3) / 1e9
+    app_gbs = abytes / (t["append_ms"] * 1e-3) / 1e9
+    dec_gbs = dbytes / (t["decode_ms"] * 1e-3) / 1e9
+    flushed = t["decode_ms_flushed"]
+    e = {
+        "workload": case.name,
+        "step_ms": round(t["step_ms"], 4), "step_GBps": round(step_gbs, 1),
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "attended_tokens_per_s": round(sum_ctx / (t["step_ms"] * 1e-3), 1),
+        "sum_context_len": sum_ctx,
+        "step_graph_replay_ms": round(t["step_graph_ms"], 4) if "step_graph_ms" in t else None,
+        "two_call_step": {"ms": round(t["two_call_step_ms"], 4),
+                          "GBps": round((dbytes + sbytes) / (t["two_call_step_ms"] * 1e-3) / 1e9, 1),
+                          "graph_replay_ms": (round(t["two_call_step_graph_ms"], 4)
+                                              if "two_call_step_graph_ms" in t else None),
+                          "calls": "pa_store_kv + pa_decode"},
+        "append_ms": round(t["append_ms"], 4),
+        "decode_ms": round(t["decode_ms"], 4),
+        "decode_ms_caches_flushed": {"median": round(float(np.median(flushed)), 4),
+                                     "min": round(float(np.min(flushed)), 4),
+                                     "max": round(float(np.max(flushed)), 4)},
+        "store_ms": round(t["store_ms"], 4),
+        "roofline": {"bound": "hbm",
+                     "kernel": f"decode_split_kernel<{g}, false, true> (pa_decode_append: the step's "
+                               "store and split-context decode with fused merge)",
+                     "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(case.name),
+                     "algorithmic_bytes_per_launch": abytes,
+                     "launch_us": round(t["append_ms"] * 1e3, 2)},
+        "pa_decode_roofline": {"bound": "hbm", "kernel": f"decode_split_kernel<{g}, false, false> (pa_decode)",
+                               "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes_per_launch": dbytes},
+        "split_plan": decode_split_plan(case, cus),
+    }
+    if ceiling is not None:
+        # the step kernel against what a load-only launch of its shape and
+        # size streams on this machine
+        e["hbm_read_ceiling_measured"] = ceiling
+        e["append_frac_of_same_size_ceiling"] = round(
+            ceiling["step_bytes"]["us"] / (t["append_ms"] * 1e3), 4)
+    return e
+
+
+DEFAULT_WORKLOAD = "long_context_decode"
+DECODE_WORKLOADS = ("long_context_decode", "qwen3_4b_decode", "qwen3_0.6b_decode")
 
 
 def main(argv=None):
@@ -708,7 +875,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_0.6b_decode", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(wl.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workload shapes")
     ap.add_argument("--no-graph", action="store_true",
@@ -754,6 +921,7 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
     pa.lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_report(args.steps, args.warmup)}), flush=True)
@@ -768,29 +936,16 @@ def main(argv=None):
           file=sys.stderr, flush=True)
     t = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
     copy_probe(args.copy_probe_mib)
-    dbytes = decode_bytes(case)
     ceiling = read_ceiling([append_bytes(case), 4 << 30], ["step_bytes", "4GiB"])
-    sbytes = store_bytes(case.batch, case.num_kv_heads)
-    abytes = append_bytes(case)
-    sum_ctx = int(case.context_lens.sum())
-    ms_step = t["step_ms"]
-    step_gbs = (dbytes + sbytes) / (ms_step * 1e-3) / 1e9
-    app_gbs = abytes / (t["append_ms"] * 1e-3) / 1e9
-    dec_gbs = dbytes / (t["decode_ms"] * 1e-3) / 1e9
-    flushed = t["decode_ms_flushed"]
-    if ceiling is not None:
-        # the step's own rate against what a load-only launch of its shape
-        # and size streams on this machine
-        ceiling["step_frac_of_step_bytes_ceiling"] = round(
-            step_gbs / ceiling["step_bytes"]["GBps"], 4)
+    head = decode_entry(case, t, cus, ceiling)
     line = {
         "metric": METRIC,
-        "value": round(step_gbs, 1),
+        "value": head.pop("step_GBps"),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head.pop("step_ms"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -798,62 +953,26 @@ def main(argv=None):
         "data": "synthetic (seeded; N(0,1) bf16 values, shuffled physical blocks)",
         "config": {"workload": case.name, "batch": case.batch, "num_q_heads": case.num_q_heads,
                    "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
-                   "block_size": case.block_size, "sum_context_len": sum_ctx,
+                   "block_size": case.block_size, "sum_context_len": int(case.context_lens.sum()),
                    "max_context_len": case.max_context_len, "num_blocks": case.num_blocks,
                    "parallelism": "single GPU"},
-        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
-        "hbm_read_ceiling_measured": ceiling,
-        "attended_tokens_per_s": round(sum_ctx / (ms_step * 1e-3), 1),
+        "roofline": head.pop("roofline"),
         "step_launch": "one pa_decode_append launch per step (store of the new tokens + decode), "
                        "launched back to back on one stream",
-        "step_graph_replay_ms": round(t["step_graph_ms"], 4) if "step_graph_ms" in t else None,
-        "two_call_step": {"ms": round(t["two_call_step_ms"], 4),
-                          "GBps": round((dbytes + sbytes) / (t["two_call_step_ms"] * 1e-3) / 1e9, 1),
-                          "graph_replay_ms": (round(t["two_call_step_graph_ms"], 4)
-                                              if "two_call_step_graph_ms" in t else None),
-                          "calls": "pa_store_kv + pa_decode"},
-        "append_ms": round(t["append_ms"], 4),
-        "decode_ms": round(t["decode_ms"], 4),
-        "decode_ms_caches_flushed": {"median": round(float(np.median(flushed)), 4),
-                                     "min": round(float(np.min(flushed)), 4),
-                                     "max": round(float(np.max(flushed)), 4)},
-        "store_ms": round(t["store_ms"], 4),
-        "roofline": {"bound": "hbm",
-                     "kernel": "decode_split_kernel<2, false, true> (pa_decode_append: the step's "
-                               "store and split-context decode with fused merge)",
-                     "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(case.name),
-                     "algorithmic_bytes_per_launch": abytes},
-        "pa_decode_roofline": {"kernel": "decode_split_kernel<2, false, false> (pa_decode)",
-                               "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                               "algorithmic_bytes_per_launch": dbytes},
+        "versions": versions(),
     }
+    head.pop("workload")
+    line.update(head)
     if not args.no_extra:
         extra = {}
-        for name in ("qwen3_4b_decode", "long_context_decode"):
+        for name in DECODE_WORKLOADS:
+            if name == case.name:
+                continue
             c = wl.CONFIGS[name]()
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             tc = time_decode(c, max(10, args.steps // 5), 3)
             cl = read_ceiling([append_bytes(c)], ["step_bytes"])
-            b, d = decode_bytes(c), tc["decode_ms"]
-            sb = store_bytes(c.batch, c.num_kv_heads)
-            extra[name] = {"decode_ms": round(d, 4), "decode_GBps": round(b / (d * 1e-3) / 1e9, 1),
-                           "decode_ms_caches_flushed_median": round(float(np.median(tc["decode_ms_flushed"])), 4),
-                           "frac_of_hbm_peak": round(b / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "attended_tokens_per_s": round(int(c.context_lens.sum()) / (d * 1e-3), 1),
-                           "append_ms": round(tc["append_ms"], 4),
-                           "append_frac_of_hbm_peak": round(append_bytes(c) / (tc["append_ms"] * 1e-3) / 1e9
-                                                            / HBM_PEAK_GBS, 4),
-                           "step_ms": round(tc["step_ms"], 4),
-                           "step_GBps": round((b + sb) / (tc["step_ms"] * 1e-3) / 1e9, 1),
-                           "two_call_step_ms": round(tc["two_call_step_ms"], 4),
-                           "append_algorithmic_bytes": append_bytes(c),
-                           "read_ceiling_same_bytes_us": cl["step_bytes"]["us"] if cl else None,
-                           "append_frac_of_same_size_ceiling": (
-                               round(cl["step_bytes"]["us"] / (tc["append_ms"] * 1e3), 4) if cl else None),
-                           "append_traffic_bytes": recorded_traffic(name),
-                           "sum_context_len": int(c.context_lens.sum())}
+            extra[name] = decode_entry(c, tc, cus, cl)
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(30, args.steps // 5), 3)
         for name in ("chunked_prefill_mixed", "multi_query_decode", "long_prefix_chunk"):
@@ -868,7 +987,14 @@ def main(argv=None):
         line["extra"] = extra
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(case)
+        line["cpu_baseline"] = cpu_baseline(case, max_seqs=2 if case.max_context_len > 65536 else 0)
+        if not args.no_extra:
+            for name in DECODE_WORKLOADS[1:]:
+                if name in line["extra"]:
+                    print(f"[bench] cpu baseline (oracle) {name}", file=sys.stderr, flush=True)
+                    line["extra"][name]["cpu_baseline"] = cpu_baseline(wl.CONFIGS[name]())
+            print("[bench] cpu baseline (oracle) prefill_8x2048", file=sys.stderr, flush=True)
+            line["extra"]["prefill_8x2048"]["cpu_baseline"] = cpu_baseline_prefill(wl.prefill_8x2048())
     print(json.dumps(line), flush=True)
     return 0
 

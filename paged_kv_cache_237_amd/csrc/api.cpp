@@ -155,18 +155,24 @@ struct PrefillSplit {
 };
 
 constexpr int64_t kPrefillSlots = 2 * 256;
+// Key tiles of the shortest split part, and parts per query block at most.
+constexpr int kPrefillSplitTiles = 16;
+constexpr int kPrefillMaxSplits = 16;
 
 PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seqlen_q,
                            int32_t num_q_heads, int32_t num_kv_heads, int group,
                            int32_t max_blocks_per_seq) {
   PrefillSplit ps;
   const int64_t max_tiles = int64_t(max_blocks_per_seq) * (PA_BLOCK_SIZE / pa::kTile);
-  ps.split_tiles = int(std::max<int64_t>(pa::kPrefillSplitTiles,
-                                         (max_tiles + pa::kPrefillMaxSplits - 1) / pa::kPrefillMaxSplits));
+  ps.split_tiles = int(std::max<int64_t>(kPrefillSplitTiles,
+                                         (max_tiles + kPrefillMaxSplits - 1) / kPrefillMaxSplits));
   const int qb = pa::kPrefillRows / group;
   ps.nqb_max = (max_seqlen_q + qb - 1) / qb;
   const int64_t slots = kPrefillSlots;
   const int64_t blocks = std::max<int64_t>(1, int64_t(batch) * num_kv_heads * ps.nqb_max);
+  // no block has more parts than its longest context has split_tiles runs
+  const int64_t cap = std::max<int64_t>(
+      1, std::min<int64_t>(kPrefillMaxSplits, (max_tiles + ps.split_tiles - 1) / ps.split_tiles));
   int64_t want = 1;
   if (2 * blocks <= slots) {
     want = slots / blocks;  // every slot once
@@ -178,11 +184,13 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
     // in one round beat 16 in two, as measured); split into the p with the
     // fewest block-times, and only when that beats one part by 30 % (304
     // blocks over 16K-token prefixes ran 21 % faster in 5 parts; 400 blocks
-    // over 8K-token prefixes were no faster in any number of parts).
+    // over 8K-token prefixes were no faster in any number of parts).  Only
+    // part counts the blocks can take are weighed: a count above `cap` would
+    // be cut back to it after the choice, where the model may predict no gain.
     constexpr double kRoundCost = 0.02;
     const double one = 1.0 + kRoundCost;
     double best = one;
-    for (int64_t p = 2; p <= pa::kPrefillMaxSplits; ++p) {
+    for (int64_t p = 2; p <= cap; ++p) {
       const double rounds = double((blocks * p + slots - 1) / slots);
       const double c = rounds * (1.0 / double(p) + kRoundCost);
       if (c < best - 1e-9) {
@@ -192,8 +200,7 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
     }
     if (best > 0.7 * one) want = 1;
   }
-  ps.max_splits = int(std::max<int64_t>(
-      1, std::min<int64_t>(want, (max_tiles + ps.split_tiles - 1) / ps.split_tiles)));
+  ps.max_splits = int(std::min<int64_t>(want, cap));
   if (ps.max_splits == 1) {
     ps.ml_bytes = ps.o_bytes = 0;
     return ps;

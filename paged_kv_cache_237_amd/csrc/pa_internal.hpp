@@ -9,12 +9,11 @@
 
 #include <string>
 
+#include "pa_common.hpp"
+#include "pa_prefill.hpp"
+
 namespace pa {
 
-constexpr int kBlock = 256;      // tokens per cache block
-constexpr int kDim = 128;        // head dim
-constexpr int kChunks = kDim / 8;  // 16-byte chunks per row
-constexpr int kTile = 64;        // decode tile: one token per lane
 
 // Partial-state record of one decode work piece: G rows of D fp32 weighted
 // values, then G maxima, then G sums (floats).
@@ -68,34 +67,6 @@ struct DecodeArgs {
   uint4* v_store;
 };
 
-struct PrefillArgs {
-  const uint16_t* q;
-  const uint4* k_cache;
-  const uint4* v_cache;
-  const int32_t* block_table;
-  const int32_t* cu_q;
-  const int32_t* ctx_lens;
-  uint16_t* out;
-  int64_t num_blocks;
-  int batch;
-  int hq;
-  int hkv;
-  int mbps;
-  int max_q;
-  float scale_log2;
-  // context split (see prefill.hip): a query block of more than split_tiles
-  // key tiles is cut into up to max_splits parts merged through the records
-  int split_tiles;
-  int max_splits;
-  int64_t total_q;   // rows the records are sized for
-  float* rec_ml;     // [max_splits][total_q][hq][2] (m, l)
-  float* rec_o;      // [max_splits][total_q][hq][kDim] unnormalised outputs
-};
-
-// Query rows per prefill workgroup, key tiles per split part, parts per block.
-constexpr int kPrefillRows = 128;
-constexpr int kPrefillSplitTiles = 16;
-constexpr int kPrefillMaxSplits = 16;
 
 struct CopyBlocksArgs {
   const int32_t* pairs;  // [n_pairs][2] (src, dst)
@@ -145,6 +116,5 @@ hipError_t check_seqs(const SeqCheckArgs& a, hipStream_t s, int* flags);
 hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t s);
 
 }  // namespace pa

@@ -45,7 +45,7 @@
 #include <math.h>
 
 #include "pa_device.hpp"
-#include "pa_internal.hpp"
+#include "pa_prefill.hpp"
 
 namespace pa {
 

@@ -34,7 +34,11 @@ def check(case, stress=False, seqs_full=None, heads_sampled=None):
     print(f"[prefill] {case.name} B={case.batch} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
           f"q_lens={case.q_lens.tolist()[:10]} ctx={case.context_lens.tolist()[:10]}", flush=True)
     dev = place(case)
-    out = bf16_out_to_f64(run_prefill(dev))
+    out_dev = run_prefill(dev)
+    # the output starts NaN-filled: a row that no workgroup (or merge) wrote
+    # shows up here, in every head, also where only some heads are compared
+    assert not torch.isnan(out_dev).any(), f"{case.name}: output rows left unwritten"
+    out = bf16_out_to_f64(out_dev)
     kp, vp = oracle_pools(case)
     q = wl.bits_to_numpy(case.q_all())
     got, ref = [], []
@@ -98,9 +102,10 @@ def test_prefill_long_prefix_split_many_ways(hq, hkv):
 
 
 def test_prefill_split_between_half_and_all_slots():
-    """A 2,160-token chunk over an 8,192-token prefix: 270 query blocks, more
-    than half the workgroup slots, so each block's keys are cut into several
-    parts that run in a few rounds, merged through the workspace."""
+    """A 2,160-token chunk over an 8,192-token prefix: 272 query blocks
+    (ceil(2160 / 64) positions-blocks x 8 kv heads at 2 q heads per kv head),
+    more than half the 512 workgroup slots, so each block's keys are cut into
+    several parts that run in a few rounds, merged through the workspace."""
     case = wl.make_case("chunk_270_blocks", "prefill", 46, [8192 + 2160], 16, 8, q_lens=[2160])
     assert pa.prefill_workspace_size(case.batch, case.total_q_rows, case.max_q_len, 16, 8,
                                      case.max_blocks_per_seq) > 0
@@ -143,7 +148,11 @@ def test_prefill_stress_peaked_softmax():
     from that rounding (see bf16_weight_bound) plus output rounding."""
     case = wl.make_case("stress", "prefill", 42, [5, 300, 700], 16, 8, q_mult=32.0)
     dev = place(case)
-    out = bf16_out_to_f64(run_prefill(dev))
+    out_dev = run_prefill(dev)
+    # the output starts NaN-filled: a row that no workgroup (or merge) wrote
+    # shows up here, in every head, also where only some heads are compared
+    assert not torch.isnan(out_dev).any(), f"{case.name}: output rows left unwritten"
+    out = bf16_out_to_f64(out_dev)
     kp, vp = oracle_pools(case)
     q = wl.bits_to_numpy(case.q_all())
     for b in range(case.batch):
