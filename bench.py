@@ -989,7 +989,7 @@ def main(argv=None):
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case, max_seqs=2 if case.max_context_len > 65536 else 0)
         if not args.no_extra:
-            for name in DECODE_WORKLOADS[1:]:
+            for name in ("qwen3_0.6b_decode",):
                 if name in line["extra"]:
                     print(f"[bench] cpu baseline (oracle) {name}", file=sys.stderr, flush=True)
                     line["extra"][name]["cpu_baseline"] = cpu_baseline(wl.CONFIGS[name]())

@@ -422,6 +422,18 @@ int pa_bm_slot_mapping(pa_block_manager* bm, int64_t seq, int64_t first_pos, int
  */
 int pa_set_debug_checks(int enabled);
 
+/*
+ * pa_set_decode_waves -- testing aid: fix the number of runs (waves) the
+ * decode calls (pa_decode, pa_decode_append, pa_decode_multi) cut their work list into, so that one input can be
+ * decoded under different split-context plans: 1 streams every (sequence,
+ * kv head) whole in one wave, larger counts cut the contexts into more
+ * partial states (at most 8 per compute unit, the count every workspace is
+ * sized for; a larger value is clamped to it).  0 (the default) restores the
+ * automatic count.  Results differ between plans by rounding only.  Applies
+ * to calls made after it, from any thread.  Returns the previous setting.
+ */
+int pa_set_decode_waves(int32_t waves);
+
 /* Name of a status code ("PA_OK", "PA_ERR_NULL_PTR", ...); never NULL. */
 const char* pa_status_string(int status);
 

@@ -40,7 +40,7 @@ EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_ap
            "pa_copy_blocks", "pa_swap_blocks", "pa_validate_block_pairs",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_allocate", "pa_bm_append",
            "pa_bm_append_batch", "pa_bm_fork", "pa_bm_free", "pa_bm_seq_len", "pa_bm_block_table", "pa_bm_slot_mapping",
-           "pa_set_debug_checks", "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
+           "pa_set_debug_checks", "pa_set_decode_waves", "pa_status_string", "pa_last_error_detail", "pa_validate_slots")
 
 
 class PAError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         l.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _i32,
                                  _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_prefill.restype = ctypes.c_int
+        l.pa_set_decode_waves.argtypes = [_i32]
+        l.pa_set_decode_waves.restype = ctypes.c_int
         l.pa_set_debug_checks.argtypes = [ctypes.c_int]
         l.pa_set_debug_checks.restype = ctypes.c_int
         l.pa_status_string.argtypes = [ctypes.c_int]
@@ -329,6 +331,12 @@ def set_debug_checks(enabled: bool) -> bool:
     """Turn the library's device-side precondition checks on or off (calls
     then synchronise their stream); returns the previous setting."""
     return bool(lib().pa_set_debug_checks(1 if enabled else 0))
+
+
+def set_decode_waves(waves: int) -> int:
+    """Testing aid: fix the number of runs the decode calls cut their work
+    into (0 = automatic); returns the previous setting."""
+    return int(lib().pa_set_decode_waves(int(waves)))
 
 
 def validate_slots(slots_host, num_slots: int) -> int:

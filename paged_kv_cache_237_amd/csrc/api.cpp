@@ -111,7 +111,14 @@ int check_geometry(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
   return PA_OK;
 }
 
+// Runs the decode's work list is cut into when set (> 0) by
+// pa_set_decode_waves, a testing aid; 0 = the automatic count.
+std::atomic<int> g_decode_waves{0};
+
 int64_t decode_waves(int cus, int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int group) {
+  const int fixed = g_decode_waves.load(std::memory_order_relaxed);
+  // every workspace is sized for kDecodeWavesPerCU waves per CU
+  if (fixed > 0) return std::min<int64_t>(fixed, int64_t(cus) * pa::kDecodeWavesPerCU);
   const int64_t tiles_upper =
       int64_t(batch) * num_kv_heads * ((int64_t(max_context_len) + pa::kTile - 1) / pa::kTile);
   // one workgroup per CU
@@ -323,6 +330,10 @@ int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, 
 }  // namespace
 
 extern "C" {
+
+int pa_set_decode_waves(int32_t waves) {
+  return g_decode_waves.exchange(waves > 0 ? waves : 0);
+}
 
 int pa_set_debug_checks(int enabled) {
   const int prev = debug_checks_on() ? 1 : 0;

@@ -117,4 +117,5 @@ hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
 
+
 }  // namespace pa

@@ -150,6 +150,15 @@ def test_decode_append_rejects_bad_arguments_on_the_host():
 
 
 @needs_lib
+def test_set_decode_waves_returns_the_previous_setting():
+    lib = pa.lib()
+    assert lib.pa_set_decode_waves(0) == 0
+    assert lib.pa_set_decode_waves(3) == 0
+    assert lib.pa_set_decode_waves(-5) == 3   # negative means automatic
+    assert lib.pa_set_decode_waves(0) == 0
+
+
+@needs_lib
 def test_decode_multi_rejects_bad_arguments_on_the_host():
     lib = pa.lib()
     base = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=4, cl=FAKE, b=2, ql=4, maxc=300,
