@@ -49,8 +49,10 @@
  *   Every array argument of a GPU call is a DEVICE pointer owned by the
  *   caller (host arrays are marked as such: the validators, pa_swap_blocks'
  *   pair list, the block manager).  The GPU calls allocate nothing; the
- *   library keeps only cached device attributes and the debug-check switch,
- *   and is thread-safe (a block manager serialises its own calls).  Every call is
+ *   library keeps only cached device attributes, the debug-check switch and
+ *   the fixed per-device scratch array of pa_decode_append_noalloc, and is
+ *   thread-safe (a block manager serialises its own calls; overlapping
+ *   pa_decode_append_noalloc calls on one device are the exception).  Every call is
  *   asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
  *   stream) on the current device.  The caller orders a store before the
  *   attention that reads it by issuing both on one stream.
@@ -200,6 +202,31 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * pa_decode_append_noalloc -- pa_decode_append without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * allocates nothing: the partial records and arrival counters live in a
+ * library-owned device array of PA_DECODE_NOALLOC_SCRATCH_BYTES bytes, which
+ * every device the library runs on holds from the library's load until the
+ * process ends.  The first call on a device clears it with a kernel on
+ * `stream` (no memset); every call leaves its counters at zero again.
+ *
+ * Same arguments (minus the workspace), results and cache writes as
+ * pa_decode_append.  A batch whose workspace (pa_decode_workspace_size)
+ * exceeds the array -- about 750 sequences at 8 kv heads and up to 4 q heads
+ * per kv head, fewer at 8 -- returns PA_ERR_WORKSPACE with nothing launched.
+ * All calls on one device share the one array: calls that overlap in time
+ * on one device (concurrent streams or threads) race and must not be made.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES 16777216
+int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                             void* stream);
 
 /*
  * pa_decode_multi -- decode of q_per_seq new tokens per sequence at once
@@ -424,7 +451,8 @@ int pa_set_debug_checks(int enabled);
 
 /*
  * pa_set_decode_waves -- testing aid: fix the number of runs (waves) the
- * decode calls (pa_decode, pa_decode_append, pa_decode_multi) cut their work list into, so that one input can be
+ * decode calls (pa_decode, pa_decode_append, pa_decode_append_noalloc,
+ * pa_decode_multi) cut their work list into, so that one input can be
  * decoded under different split-context plans: 1 streams every (sequence,
  * kv head) whole in one wave, larger counts cut the contexts into more
  * partial states (at most 8 per compute unit, the count every workspace is

@@ -34,6 +34,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
+           "pa_decode_append_noalloc",
            "pa_decode_multi_workspace_size",
            "pa_decode_multi", "pa_prefill_workspace_size",
            "pa_prefill",
@@ -78,6 +79,9 @@ def lib() -> ctypes.CDLL:
         l.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _i64, _f32, _vp, _sz, _vp]
         l.pa_decode_append.restype = ctypes.c_int
+        l.pa_decode_append_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i64, _f32, _vp]
+        l.pa_decode_append_noalloc.restype = ctypes.c_int
         l.pa_decode_multi_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
         l.pa_decode_multi_workspace_size.restype = _sz
         l.pa_decode_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
@@ -249,6 +253,30 @@ def decode_append(out, q, k_new, v_new, k_cache, v_cache, block_table, context_l
         int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         _dev(workspace, "workspace", (torch.uint8, torch.float32, torch.int32)),
         workspace.numel() * workspace.element_size(), _stream(q, stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16777216
+
+
+def decode_append_noalloc(out, q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                          max_context_len: int, scale: float, stream=None) -> None:
+    """pa_decode_append_noalloc: pa_decode_append with the library's own
+    per-device scratch instead of a workspace (nothing is allocated; calls
+    that overlap in time on one device must not be made)."""
+    nb, hkv = _cache_geometry(k_cache, v_cache)
+    b, hq, d = (int(x) for x in q.shape)
+    if tuple(out.shape) != (b, hq, d) or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("shape mismatch between q, out and block_table")
+    if tuple(context_lens.shape) != (b,):
+        raise ValueError("context_lens must be [B]")
+    if tuple(k_new.shape) != (b, hkv, d) or tuple(v_new.shape) != (b, hkv, d):
+        raise ValueError("k_new and v_new must be [B, Hkv, 128]")
+    _check(lib().pa_decode_append_noalloc(
+        _dev(out, "out", _BF16), _dev(q, "q", _BF16), _dev(k_new, "k_new", _BF16),
+        _dev(v_new, "v_new", _BF16), _dev(k_cache, "k_cache", _BF16),
+        _dev(v_cache, "v_cache", _BF16), _dev(block_table, "block_table", _I32),
+        int(block_table.shape[1]), _dev(context_lens, "context_lens", _I32), b,
+        int(max_context_len), hq, hkv, d, BLOCK_SIZE, nb, float(scale), _stream(q, stream)))
 
 
 def decode_multi_workspace_size(batch: int, q_per_seq: int, num_q_heads: int,

@@ -229,12 +229,15 @@ int virtual_group(int group, int32_t q_per_seq) {
 
 // Decode of q_per_seq query rows per sequence (1 for pa_decode); with k_new
 // set (one row per sequence), the newest position of each sequence is the
-// appended token (pa_decode_append) and the caches are written.
+// appended token (pa_decode_append) and the caches are written.  With
+// noalloc, the workspace is the library's per-device scratch, looked up once
+// every argument has been checked.
 int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
                 const void* v_cache, const int32_t* block_table, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, int32_t batch, int32_t q_per_seq, int32_t max_context_len,
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes, void* stream,
+                bool noalloc = false) {
   try {
     if (batch < 0) return fail(PA_ERR_BAD_SHAPE, "batch < 0");
     int group = 0;
@@ -271,6 +274,16 @@ int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, 
     if (r != PA_OK) return r;
     const int64_t waves = decode_waves(cus, batch, num_kv_heads, max_context_len, gv);
     const size_t need = decode_ws_bytes(batch, num_kv_heads, gv, waves);
+    if (noalloc) {
+      if (need > pa::kNoAllocScratchBytes)
+        return fail(PA_ERR_WORKSPACE, "pa_decode_append_noalloc: this batch needs " + std::to_string(need) +
+                                          " bytes of workspace, more than the library's " +
+                                          std::to_string(pa::kNoAllocScratchBytes) +
+                                          "-byte scratch; use pa_decode_append with a workspace");
+      const hipError_t se = pa::noalloc_scratch(static_cast<hipStream_t>(stream), &workspace);
+      if (se != hipSuccess) return hip_fail(se, "decode scratch lookup");
+      workspace_bytes = pa::kNoAllocScratchBytes;
+    }
     if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
     if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
@@ -583,6 +596,21 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
   return decode_rows(out, q, k_new, v_new, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
                      batch, 1, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      scale, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                             void* stream) {
+  static_assert(pa::kNoAllocScratchBytes == PA_DECODE_NOALLOC_SCRATCH_BYTES,
+                "scratch size differs from the header's");
+  if (batch > 0 && (k_new == nullptr || v_new == nullptr))
+    return fail(PA_ERR_NULL_PTR, "pa_decode_append_noalloc: k_new or v_new is NULL");
+  return decode_rows(out, q, k_new, v_new, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
+                     batch, 1, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     scale, nullptr, 0, stream, true);
 }
 
 int pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -67,6 +67,9 @@
 // out; the kernel is bound by HBM bandwidth.
 #include <math.h>
 
+#include <mutex>
+#include <vector>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -832,6 +835,48 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
                        s, a);
   }
   return hipGetLastError();
+}
+
+// Workspace of the allocation-free decode step (pa_decode_append_noalloc),
+// for callers that cannot allocate device memory: the same partial records
+// and arrival counters as a caller's workspace, in an array of fixed size
+// that each device holds from the library's load until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only
+// names the symbol); it uses the device address that hipGetSymbolAddress
+// returns, found once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+__global__ __launch_bounds__(256) void zero16_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t noalloc_scratch(hipStream_t s, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device; null until looked up
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && size_t(dev) < addr.size() && addr[dev] != nullptr) {
+    *ptr = addr[dev];
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+  // The counters must start at zero: the whole array is cleared once, by a
+  // kernel on the caller's stream (no memset node, in case the stream is
+  // being captured); every call leaves its counters at zero again.
+  hipLaunchKernelGGL(zero16_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p),
+                     int64_t(kNoAllocScratchBytes / 16));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (size_t(dev) >= addr.size()) addr.resize(size_t(dev) + 1, nullptr);
+  addr[dev] = p;
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s) {

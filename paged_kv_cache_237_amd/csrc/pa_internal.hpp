@@ -117,5 +117,12 @@ hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
 
+// Library-owned decode workspace of the allocation-free decode step: the
+// bytes of the per-device array (decode.hip), and its device address on the
+// current device, found once per device and cleared on `s` at that first
+// use (later calls find it as the previous call left it: records are
+// scratch, counters are back at zero).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
 
 }  // namespace pa

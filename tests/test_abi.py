@@ -150,6 +150,35 @@ def test_decode_append_rejects_bad_arguments_on_the_host():
 
 
 @needs_lib
+def test_decode_append_noalloc_rejects_bad_arguments_on_the_host():
+    """The allocation-free step checks its arguments like pa_decode_append,
+    before it looks up (or clears) its scratch on the device."""
+    lib = pa.lib()
+    base = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=4, cl=FAKE, b=2,
+                maxc=300, hq=16, hkv=8, d=128, bs=256, nb=8, scale=0.088)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return no_launch(lib.pa_decode_append_noalloc(
+            a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["mbps"], a["cl"], a["b"],
+            a["maxc"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], None))
+
+    assert call(b=0) == 0
+    assert call(b=0, kn=None) == 0
+    assert call(kn=None) == -1
+    assert call(vn=None) == -1
+    assert call(b=-1) == -2
+    assert call(hq=24) == -3
+    assert call(d=64) == -3
+    assert call(bs=128) == -3
+    assert call(maxc=4 * 256 + 1) == -2
+    assert call(scale=float("inf")) == -2
+    assert call(q=None) == -1
+    assert call(kn=FAKE + 8) == -4
+    assert call(out=FAKE + 8) == -4
+
+
+@needs_lib
 def test_set_decode_waves_returns_the_previous_setting():
     lib = pa.lib()
     assert lib.pa_set_decode_waves(0) == 0
