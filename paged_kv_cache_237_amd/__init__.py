@@ -20,7 +20,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIB_PATH selects another build of the library (the host-only sanitizer
+# build that tests/test_host_sanitizers.py runs the CPU suites against).
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libpa.so")
 
 BLOCK_SIZE = 256
 HEAD_DIM = 128
