@@ -345,11 +345,13 @@ def varlen_report(name: str, steps: int, warmup: int) -> dict:
             "store_ms": round(sto, 4)}
 
 
-def decode_multi_report(steps: int, warmup: int) -> dict:
-    """pa_decode_multi on the multi-query decode workload (4 new tokens per
-    sequence scored in one pass): the K/V bytes of every context read once,
-    over the HBM peak."""
-    c = wl.multi_query_decode()
+def decode_multi_report(name: str, steps: int, warmup: int) -> dict:
+    """pa_decode_multi on a multi-query decode workload (several new tokens
+    per sequence scored in one pass: the vector-ALU kernel up to 8 rows per
+    (sequence, kv head), the matrix-core kernel for 9 to 32): the algorithmic
+    bytes (every context's K/V rows once, q in, out written, table entries,
+    lengths) over the HBM peak, HIP events around single launches."""
+    c = wl.CONFIGS[name]()
     ql = int(c.q_lens[0])
     dev = place(c)
     pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
@@ -370,14 +372,21 @@ def decode_multi_report(steps: int, warmup: int) -> dict:
         call()
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     kvb = int(c.context_lens.sum()) * c.num_kv_heads * c.head_dim * 2 * 2
-    gbs = kvb / (ms * 1e-3) / 1e9
+    blocks = sum(wl.blocks_for(int(n)) for n in c.context_lens)
+    alg = kvb + 2 * c.total_q_rows * c.num_q_heads * c.head_dim * 2 + 4 * blocks + 4 * c.batch
+    gbs = alg / (ms * 1e-3) / 1e9
+    rows = ql * c.num_q_heads // c.num_kv_heads
+    kernel = "decode_mfma_kernel" if rows > 8 else "decode_split_kernel (several rows)"
     del dev, out, ws
     torch.cuda.empty_cache()
     return {"workload": c.name, "entry_point": "pa_decode_multi", "q_per_seq": ql,
-            "decode_ms": round(ms, 4), "kv_GBps": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "rows_per_kv_head": rows, "decode_ms": round(ms, 4), "kv_GBps": round(kvb / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": alg}}
 
 
 def blocks_report(steps: int, warmup: int) -> dict:
@@ -975,11 +984,13 @@ def main(argv=None):
             extra[name] = decode_entry(c, tc, cus, cl)
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(30, args.steps // 5), 3)
-        for name in ("chunked_prefill_mixed", "multi_query_decode", "long_prefix_chunk"):
+        for name in ("chunked_prefill_mixed", "multi_query_decode", "spec_verify_decode",
+                     "long_prefix_chunk"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(30, args.steps // 5), 3)
-        print("[bench] extra multi-query decode (pa_decode_multi)", file=sys.stderr, flush=True)
-        extra["multi_query_decode_multi"] = decode_multi_report(max(10, args.steps // 5), 3)
+        for name in ("multi_query_decode", "spec_verify_decode"):
+            print(f"[bench] extra {name} (pa_decode_multi)", file=sys.stderr, flush=True)
+            extra[f"{name}_multi"] = decode_multi_report(name, max(20, args.steps // 5), 3)
         print("[bench] extra block copy / swap", file=sys.stderr, flush=True)
         extra["blocks"] = blocks_report(max(10, args.steps // 5), 3)
         print("[bench] extra block manager (host)", file=sys.stderr, flush=True)

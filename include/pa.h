@@ -242,17 +242,20 @@ int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const 
  *
  *   out, q        : bf16 [batch * q_per_seq][num_q_heads][head_dim], row
  *                   b * q_per_seq + i, 16-B aligned.
- *   q_per_seq     : 1 .. 8, with q_per_seq * num_q_heads / num_kv_heads <= 8
+ *   q_per_seq     : 1 .. 32, with q_per_seq * num_q_heads / num_kv_heads <= 32
  *                   (else PA_ERR_UNSUPPORTED): the rows of one (sequence, kv
- *                   head) are processed together like the query heads of one
- *                   kv head in pa_decode.
+ *                   head) are processed together -- up to 8 like the query
+ *                   heads of one kv head in pa_decode, 9 to 32 as one block
+ *                   of 32 rows on the matrix cores (P rounded to bf16 before
+ *                   P.V, as in pa_prefill).
  *   context_lens  : int32 [batch], each >= q_per_seq for meaningful rows (a
  *                   row whose position is negative sees no key and is zero).
  *   workspace     : >= pa_decode_multi_workspace_size(...) bytes; same rules
  *                   as pa_decode's workspace.
  *   Other arguments as for pa_decode.
- *   Source: CSDN essay, first and third sections (the decode kernel); the
- *   causal rule of the prefill description on the same pages.
+ *   Source: CSDN essay, first and third sections (the decode kernel), and
+ *   its section on speculative decoding (drafted tokens checked in one
+ *   pass); the causal rule of the prefill description on the same pages.
  */
 size_t pa_decode_multi_workspace_size(int32_t batch, int32_t q_per_seq, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size);

@@ -287,7 +287,7 @@ def decode_multi_workspace_size(batch: int, q_per_seq: int, num_q_heads: int,
     n = lib().pa_decode_multi_workspace_size(batch, q_per_seq, num_q_heads, num_kv_heads, HEAD_DIM,
                                              BLOCK_SIZE)
     if n == 0 and batch > 0:
-        raise PAError(-3, "no workspace size for these shapes (q_per_seq * Hq/Hkv must be <= 8)")
+        raise PAError(-3, "no workspace size for these shapes (q_per_seq * Hq/Hkv must be <= 32)")
     return int(n)
 
 

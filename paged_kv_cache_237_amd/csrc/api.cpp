@@ -219,12 +219,17 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
 }
 
 // Virtual heads per (sequence, kv head) of a decode of q_per_seq rows: group
-// * q_per_seq rounded up to a power of two; 0 if that exceeds 8.
+// * q_per_seq rounded up to a power of two when that is at most 8 (the
+// vector-ALU kernel), 32 for 9 to 32 rows (the matrix-core kernel), 0 beyond.
+constexpr int kMfmaRows = 32;
 int virtual_group(int group, int32_t q_per_seq) {
-  if (q_per_seq < 1 || q_per_seq > 8) return 0;
+  if (q_per_seq < 1 || q_per_seq > kMfmaRows) return 0;
+  const int rows = group * q_per_seq;
+  if (rows > kMfmaRows) return 0;
+  if (rows > 8) return kMfmaRows;
   int gv = 1;
-  while (gv < group * q_per_seq) gv *= 2;
-  return gv <= 8 ? gv : 0;
+  while (gv < rows) gv *= 2;
+  return gv;
 }
 
 // Decode of q_per_seq query rows per sequence (1 for pa_decode); with k_new
@@ -246,7 +251,7 @@ int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, 
     if (q_per_seq < 1) return fail(PA_ERR_BAD_SHAPE, "q_per_seq must be >= 1");
     const int gv = virtual_group(group, q_per_seq);
     if (gv == 0)
-      return fail(PA_ERR_UNSUPPORTED, "q_per_seq * num_q_heads / num_kv_heads must be at most 8");
+      return fail(PA_ERR_UNSUPPORTED, "q_per_seq * num_q_heads / num_kv_heads must be at most 32");
     if (max_blocks_per_seq <= 0) return fail(PA_ERR_BAD_SHAPE, "max_blocks_per_seq must be positive");
     if (num_blocks <= 0) return fail(PA_ERR_BAD_SHAPE, "num_blocks must be positive");
     if (max_context_len < 0 || int64_t(max_context_len) > int64_t(max_blocks_per_seq) * PA_BLOCK_SIZE)
@@ -332,7 +337,8 @@ int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, 
       if (ce != hipSuccess) return hip_fail(ce, "decode checks");
       if (flags) return precondition_fail(flags);
     }
-    const hipError_t e = pa::launch_decode(a, gv, static_cast<hipStream_t>(stream));
+    const hipError_t e = gv == kMfmaRows ? pa::launch_decode_mfma(a, static_cast<hipStream_t>(stream))
+                                         : pa::launch_decode(a, gv, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
   } catch (...) {

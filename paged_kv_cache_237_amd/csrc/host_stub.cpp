@@ -16,6 +16,7 @@ hipError_t check_seqs(const SeqCheckArgs&, hipStream_t, int*) { return hipErrorN
 hipError_t launch_store_kv(const StoreArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_copy_blocks(const CopyBlocksArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(const DecodeArgs&, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefill(const PrefillArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t noalloc_scratch(hipStream_t, void**) { return hipErrorNoDevice; }
 

@@ -314,12 +314,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int t_end = int(int64_t(ntiles) * (part + 1) / nsplit);
 
   // Q^T operand: dims 16*ks + 8*half .. +7 of the lane's row, 8 k-steps.
+  // With a negative scale the sign goes into q (exact in bf16), so scores are
+  // scaled by a positive factor and a row's largest score is its largest
+  // weight (the row max below relies on that).
   bf16x8_t qop[8];
   {
     const uint4* qrow = reinterpret_cast<const uint4*>(
         a.q + (int64_t(q0) + (row_ok ? pos : 0)) * (int64_t(a.hq) * kDim) + int64_t(head) * kDim);
+    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(row_ok ? qrow[2 * ks + half] : zero4());
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 u = row_ok ? qrow[2 * ks + half] : zero4();
+      u.x ^= flip;
+      u.y ^= flip;
+      u.z ^= flip;
+      u.w ^= flip;
+      qop[ks] = as_bf16x8(u);
+    }
   }
 
   // Tile t+1 is loaded into registers while tile t is computed from LDS;
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     load_v(a, table, g, ctx, t_begin, tid, vr);
   }
 
-  const float c = a.scale_log2;
+  const float c = fabsf(a.scale_log2);
   f32x16_t o[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n)

@@ -202,15 +202,18 @@ def test_decode_multi_rejects_bad_arguments_on_the_host():
 
     assert call(b=0) == 0
     assert call(ql=0) == -2
-    assert call(ql=5) == -3           # 2 heads x 5 rows: 16 virtual heads
-    assert call(ql=9) == -3
-    assert call(hq=64, ql=2) == -3    # G = 8 leaves room for one row only
+    assert call(ql=17) == -3          # 2 heads x 17 rows: 34 rows per kv head
+    assert call(ql=33) == -3
+    assert call(hq=64, ql=5) == -3    # G = 8 leaves room for 4 rows
     assert call(hq=24) == -3          # G = 3
     assert call(maxc=-1) == -2
     assert call(q=None) == -1
     assert call(out=FAKE + 8) == -4
+    assert call(ql=6, out=FAKE + 8) == -4  # the matrix-core kernel's rows check alike
+    assert call(ql=6, maxc=-1) == -2
     assert lib.pa_decode_multi_workspace_size(2, 0, 16, 8, 128, 256) == 0
-    assert lib.pa_decode_multi_workspace_size(2, 5, 16, 8, 128, 256) == 0
+    assert lib.pa_decode_multi_workspace_size(2, 17, 16, 8, 128, 256) == 0
+    assert lib.pa_decode_multi_workspace_size(2, 5, 64, 8, 128, 256) == 0
 
 
 @needs_lib

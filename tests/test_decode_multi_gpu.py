@@ -51,7 +51,11 @@ def test_multi_query_decode_workload():
 
 
 @pytest.mark.parametrize("hq,hkv,ql", [(8, 8, 8), (8, 8, 3), (8, 8, 1), (16, 8, 4), (16, 8, 3),
-                                       (16, 8, 2), (32, 8, 2), (64, 8, 1), (4, 1, 2)])
+                                       (16, 8, 2), (32, 8, 2), (64, 8, 1), (4, 1, 2),
+                                       # 9..32 rows per (sequence, kv head): the matrix-core kernel
+                                       (16, 8, 5), (16, 8, 6), (32, 8, 5), (32, 8, 6), (32, 8, 3),
+                                       (32, 8, 8), (64, 8, 4), (64, 8, 2), (8, 8, 9), (8, 8, 32),
+                                       (4, 1, 8)])
 def test_decode_multi_group_and_row_counts(hq, hkv, ql):
     ctx = [ql, ql + 1, 63, 64, 65, 255, 257, 700, 1500]
     case = wl.make_case(f"multi_{hq}_{hkv}_{ql}", "prefill", 60 + hq + ql, ctx, hq, hkv,
@@ -84,3 +88,43 @@ def test_decode_multi_matches_prefill():
                dev.block_table, case.scale, ws)
     torch.cuda.synchronize()
     assert np.abs(bf16_out_to_f64(out) - multi).max() <= 2 * 1.5e-2
+
+
+def test_speculative_verification_workload():
+    """64 sequences each verify 5 drafted tokens plus the next one (6 rows)
+    over U{512..4096} cached tokens: 12 rows per (sequence, kv head), the
+    matrix-core kernel."""
+    check(wl.spec_verify_decode(), 6)
+
+
+@pytest.mark.parametrize("hq", [16, 32])
+def test_decode_multi_many_rows_matches_prefill(hq):
+    """The same rows through pa_prefill (a varlen batch with q_len = 6 and a
+    cached prefix): both within the oracle bar and close to each other."""
+    lens = [6, 7, 100, 300, 1000, 2000, 4097]
+    case = wl.make_case(f"multi_vs_prefill_{hq}", "prefill", 80 + hq, lens, hq, 8, q_lens=[6] * len(lens))
+    _, dev, multi = check(case, 6)
+    out = torch.empty((case.total_q_rows, hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len, hq, 8,
+                                    case.max_blocks_per_seq)
+    pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache, dev.v_cache,
+               dev.block_table, case.scale, ws)
+    torch.cuda.synchronize()
+    pre = bf16_out_to_f64(out)
+    assert np.abs(multi - pre).max() <= 1.5e-2
+
+
+def test_decode_multi_long_contexts_cut_across_waves():
+    """Few long sequences with 6 rows at 32 q / 8 kv heads: every segment is
+    cut into many runs and merged from 32-row partial records (sampled
+    sequences against the oracle)."""
+    case = wl.make_case("multi_long", "prefill", 88, [40000, 70001, 6, 9000], 32, 8, q_lens=[6] * 4)
+    check(case, 6)
+
+
+def test_decode_multi_negative_scale():
+    """A negative logit scale (allowed: finite) on both decode-multi kernels."""
+    for hq, ql in ((16, 2), (32, 6)):
+        case = wl.make_case(f"multi_negscale_{hq}", "prefill", 90 + hq, [ql, 70, 700, 3000], hq, 8,
+                            q_lens=[ql] * 4, scale=-0.09)
+        check(case, ql)

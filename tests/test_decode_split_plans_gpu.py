@@ -72,3 +72,34 @@ def test_split_plans_agree_with_oracle_and_ignore_placement(hq, append):
     # one wave per context and the automatic plan really are different cuts:
     # their results differ somewhere by rounding (else the knob did nothing)
     assert not torch.equal(outs[1], outs[1 << 20])
+
+
+@pytest.mark.parametrize("hq,ql", [(16, 6), (32, 5)])
+def test_multi_row_split_plans(hq, ql):
+    """pa_decode_multi with 12 or 20 rows per (sequence, kv head) -- the
+    matrix-core kernel, whose partial records hold 32 rows -- under the same
+    plans, against the oracle's causal attention."""
+    case = wl.make_case(f"plans_multi_{hq}", "prefill", 140 + hq, [ql, 63 + ql, 700, 3000, 4096, 257],
+                        hq, 8, q_lens=[ql] * 6, num_blocks=40)
+    dev = place(case)
+    pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+    kp, vp = oracle_pools(case)
+    q = wl.bits_to_numpy(case.q_all())
+    ref = np.concatenate([oracle.prefill_seq(q[b * ql:(b + 1) * ql], kp, vp, case.block_table[b],
+                                             int(case.context_lens[b]), case.scale)
+                          for b in range(case.batch)])
+    ws = pa.alloc_decode_multi_workspace(case.batch, ql, hq, 8)
+    outs = {}
+    try:
+        for waves in PLANS:
+            print(f"[plans multi] hq={hq} ql={ql} waves={waves}", flush=True)
+            pa.set_decode_waves(waves)
+            out = torch.full((case.batch * ql, hq, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+            pa.decode_multi(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens, ql,
+                            case.max_context_len, case.scale, ws)
+            torch.cuda.synchronize()
+            compare(bf16_out_to_f64(out), ref, f"plans multi hq={hq} waves={waves}")
+            outs[waves] = out.view(torch.int16).clone()
+    finally:
+        pa.set_decode_waves(0)
+    assert not torch.equal(outs[1], outs[1 << 20])

@@ -348,6 +348,16 @@ def multi_query_decode() -> PagedCase:
                      q_lens=np.full(64, 4, dtype=np.int64), rng=rng)
 
 
+def spec_verify_decode() -> PagedCase:
+    """Speculative verification with 5 drafted tokens: 64 sequences each score
+    the 5 drafted tokens and the next one (6 new tokens) over U{512..4096}
+    cached tokens, causally among themselves; 16 q / 8 kv heads."""
+    rng = np.random.default_rng(9)
+    ctx = rng.integers(512, 4096, size=64, endpoint=True)
+    return make_case("spec_verify_decode", "prefill", 9, ctx, 16, 8,
+                     q_lens=np.full(64, 6, dtype=np.int64), rng=rng)
+
+
 def long_prefix_chunk() -> PagedCase:
     """One long prompt mid-way through chunked prefill: a 512-token chunk on
     top of a 65,536-token cached prefix, one sequence; 16 q / 8 kv heads."""
@@ -363,6 +373,7 @@ CONFIGS = {
     "chunked_prefill_mixed": chunked_prefill_mixed,
     "multi_query_decode": multi_query_decode,
     "long_prefix_chunk": long_prefix_chunk,
+    "spec_verify_decode": spec_verify_decode,
 }
 
 
