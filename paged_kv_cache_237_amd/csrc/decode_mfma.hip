@@ -172,48 +172,67 @@ __device__ __forceinline__ void mf_load_q(const DecodeArgs& a, int b, int g, uin
 
 // Merge of the partial records of segment seg written by waves w0..w1: for
 // every real row, M = max m_i, L = sum 2^(m_i - M) l_i, o = sum 2^(m_i - M)
-// O_i / L; lane = 2 dims.  Rows go 8 at a time; the loads of one record for
-// those rows are issued together.
+// O_i / L.  Lane = 4 dims (4 (lane % 32) ..) of 16 rows (16 (lane / 32) ..);
+// a record is one round of loads (16-byte reads, each half-wave covering a
+// row's 512 bytes), and the next record's loads are issued before the
+// current one is folded in.
+struct MfRecPart {
+  float m[16], l[16];
+  float4 u[16];
+};
+
+__device__ __forceinline__ void mf_load_rec(const DecodeArgs& a, int rec_idx, int rh, int d0, MfRecPart& p) {
+  const float* rec = a.ws + int64_t(rec_idx) * partial_floats(kMfRows);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, uint32_t(partial_floats(kMfRows)) * 4u);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p.m[r] = ld_coherent(rec + kMfRows * kDim + rh + r);
+    p.l[r] = ld_coherent(rec + kMfRows * kDim + kMfRows + rh + r);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rr, int(uint32_t((rh + r) * kDim + d0) * 4u), 0,
+                                                             kCpolAgent);
+    const unsigned x = v.x, y = v.y, z = v.z, w = v.w;
+    p.u[r] = make_float4(__uint_as_float(x), __uint_as_float(y), __uint_as_float(z), __uint_as_float(w));
+  }
+}
+
 __device__ void mf_merge(const DecodeArgs& a, int seg, int b, int g, int w0, int w1) {
-  constexpr int kR = 8;
   const int lane = lane_id();
+  const int d0 = 4 * (lane & 31), rh = 16 * (lane >> 5);
   const int nreal = min(kMfRows, a.ql << a.gr_shift);
-  for (int r0 = 0; r0 < nreal; r0 += kR) {
-    float M[kR], L[kR], U0[kR], U1[kR];
+  float M[16], L[16];
+  float4 U[16];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      M[r] = -INFINITY;
-      L[r] = U0[r] = U1[r] = 0.f;
+  for (int r = 0; r < 16; ++r) {
+    M[r] = -INFINITY;
+    L[r] = 0.f;
+    U[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  MfRecPart cur;
+  mf_load_rec(a, seg + w0, rh, d0, cur);
+  for (int w = w0; w <= w1; ++w) {
+    MfRecPart nxt;
+    if (w < w1) mf_load_rec(a, seg + w + 1, rh, d0, nxt);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float mn = fmaxf(M[r], cur.m[r]);
+      const float ref = mn == -INFINITY ? 0.f : mn;
+      const float sa = __builtin_amdgcn_exp2f(M[r] - ref);
+      const float sb = __builtin_amdgcn_exp2f(cur.m[r] - ref);
+      L[r] = L[r] * sa + cur.l[r] * sb;
+      U[r].x = U[r].x * sa + cur.u[r].x * sb;
+      U[r].y = U[r].y * sa + cur.u[r].y * sb;
+      U[r].z = U[r].z * sa + cur.u[r].z * sb;
+      U[r].w = U[r].w * sa + cur.u[r].w * sb;
+      M[r] = mn;
     }
-    for (int w = w0; w <= w1; ++w) {
-      const float* rec = a.ws + int64_t(seg + w) * partial_floats(kMfRows);
-      const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, uint32_t(partial_floats(kMfRows)) * 4u);
-      float mm[kR], ll[kR], ua[kR], ub[kR];
+    if (w < w1) cur = nxt;
+  }
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        mm[r] = ld_coherent(rec + kMfRows * kDim + r0 + r);
-        ll[r] = ld_coherent(rec + kMfRows * kDim + kMfRows + r0 + r);
-        ld_coherent2(rr, uint32_t((r0 + r) * kDim + 2 * lane) * 4u, ua[r], ub[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const float mn = fmaxf(M[r], mm[r]);
-        const float ref = mn == -INFINITY ? 0.f : mn;
-        const float sa = __builtin_amdgcn_exp2f(M[r] - ref);
-        const float sb = __builtin_amdgcn_exp2f(mm[r] - ref);
-        L[r] = L[r] * sa + ll[r] * sb;
-        U0[r] = U0[r] * sa + ua[r] * sb;
-        U1[r] = U1[r] * sa + ub[r] * sb;
-        M[r] = mn;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      if (r0 + r >= nreal) break;
-      const float inv = L[r] > 0.f ? 1.f / L[r] : 0.f;
-      uint32_t* out = reinterpret_cast<uint32_t*>(a.out + vrow<kMfRows, true>(a, b, g, r0 + r) * kDim);
-      out[lane] = pack_bf16x2(U0[r] * inv, U1[r] * inv);
-    }
+  for (int r = 0; r < 16; ++r) {
+    if (rh + r >= nreal) break;
+    const float inv = L[r] > 0.f ? 1.f / L[r] : 0.f;
+    uint2* out = reinterpret_cast<uint2*>(a.out + vrow<kMfRows, true>(a, b, g, rh + r) * kDim + d0);
+    *out = make_uint2(pack_bf16x2(U[r].x * inv, U[r].y * inv), pack_bf16x2(U[r].z * inv, U[r].w * inv));
   }
 }
 
