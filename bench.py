@@ -85,14 +85,15 @@ def read_ceiling(sizes, labels, steps: int = 30) -> dict:
     launch (one 8-wave workgroup per CU, each wave streaming contiguous 32 KiB
     pieces; csrc/read_ceiling.hip), for each byte count in `sizes` (rounded
     down to 32 KiB): what a launch of that shape and size can stream on this
-    machine, reported beside the vendor peak.  None if the probe library is
-    not built."""
+    machine, reported beside the vendor peak -- with the default cache policy
+    and with the non-temporal one the decode kernels use ("nt").  None if the
+    probe library is not built."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
         return None
     lib = ctypes.CDLL(PROBE_LIB)
     lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                         ctypes.c_void_p, ctypes.c_void_p]
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.pa_probe_stream_read.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sizes = [int(n) // 32768 * 32768 for n in sizes]
@@ -101,16 +102,18 @@ def read_ceiling(sizes, labels, steps: int = 30) -> dict:
     stream = torch.cuda.current_stream()
     res = {"kernel": "stream_read_kernel (load-only, decode launch shape)", "workgroups": cus}
     for n, label in zip(sizes, labels):
-        def call():
-            st = lib.pa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), n, cus,
-                                          ctypes.c_void_p(sink.data_ptr()),
-                                          ctypes.c_void_p(stream.cuda_stream))
-            if st != 0:
-                raise RuntimeError(f"pa_probe_stream_read returned {st}")
-        _warm(call, 20)
-        _, ts = _events_ms(call, steps)
-        ms = float(np.median(ts))
-        res[label] = {"bytes": n, "us": round(ms * 1e3, 2), "GBps": round(n / (ms * 1e-3) / 1e9, 1)}
+        for nt in (0, 1):
+            def call():
+                st = lib.pa_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), n, cus, nt,
+                                              ctypes.c_void_p(sink.data_ptr()),
+                                              ctypes.c_void_p(stream.cuda_stream))
+                if st != 0:
+                    raise RuntimeError(f"pa_probe_stream_read returned {st}")
+            _warm(call, 20)
+            _, ts = _events_ms(call, steps)
+            ms = float(np.median(ts))
+            res[label + ("_nt" if nt else "")] = {"bytes": n, "us": round(ms * 1e3, 2),
+                                                  "GBps": round(n / (ms * 1e-3) / 1e9, 1)}
     del buf, sink
     torch.cuda.empty_cache()
     return res
@@ -868,10 +871,10 @@ def decode_entry(case: wl.PagedCase, t: dict, cus: int, ceiling=None) -> dict:
     }
     if ceiling is not None:
         # the step kernel against what a load-only launch of its shape and
-        # size streams on this machine
+        # size streams on this machine (non-temporal loads, as the kernel's)
         e["hbm_read_ceiling_measured"] = ceiling
         e["append_frac_of_same_size_ceiling"] = round(
-            ceiling["step_bytes"]["us"] / (t["append_ms"] * 1e3), 4)
+            ceiling["step_bytes_nt"]["us"] / (t["append_ms"] * 1e3), 4)
     return e
 
 

@@ -238,12 +238,12 @@ __device__ __forceinline__ TileLoads tile_loads(const DecodeArgs& a, int phys, i
 
 __device__ __forceinline__ void issue_k(const TileLoads& tl, uint4 (&kr)[kChunks]) {
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) kr[c] = buf_load16(tl.rk, tl.koff, uint32_t(c) * 4096u);
+  for (int c = 0; c < kChunks; ++c) kr[c] = buf_load16_stream(tl.rk, tl.koff, uint32_t(c) * 4096u);
 }
 
 __device__ __forceinline__ void issue_v(const TileLoads& tl, uint4 (&vr)[16]) {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) vr[k] = buf_load16(tl.rv, tl.voff + uint32_t(k) * 1024u, 0u);
+  for (int k = 0; k < 16; ++k) vr[k] = buf_load16_stream(tl.rv, tl.voff + uint32_t(k) * 1024u, 0u);
 }
 
 // Streams tiles [pos, end) of the flattened list (this wave's run) as one

@@ -110,7 +110,7 @@ __device__ __forceinline__ void mf_issue_k(const MfTile& tl, uint4 (&kr)[16]) {
     const int key = 32 * ms + col;
     const uint32_t off = key < tl.valid ? uint32_t(tl.r0 + key) * 16u + uint32_t(half) * 4096u : kOutOfRange;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kr[8 * ms + ks] = buf_load16(tl.rk, off + uint32_t(ks) * 8192u, 0u);
+    for (int ks = 0; ks < 8; ++ks) kr[8 * ms + ks] = buf_load16_stream(tl.rk, off + uint32_t(ks) * 8192u, 0u);
   }
 }
 
@@ -122,7 +122,7 @@ __device__ __forceinline__ void mf_issue_v(const MfTile& tl, uint4 (&vr)[16]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[4 * j + i] = buf_load16(tl.rv, base + uint32_t(16 * j + i) * 256u, 0u);
+    for (int i = 0; i < 4; ++i) vr[4 * j + i] = buf_load16_stream(tl.rv, base + uint32_t(16 * j + i) * 256u, 0u);
 }
 
 // The tile's V into LDS as [dim][key], each 16 keys in the order the P
