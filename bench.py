@@ -348,6 +348,94 @@ def varlen_report(name: str, steps: int, warmup: int) -> dict:
             "store_ms": round(sto, 4)}
 
 
+def mixed_split_report(steps: int, warmup: int) -> dict:
+    """The chunked-prefill step mixed with decode rows (64 one-token rows over
+    U{512..4096} + 8 x 512-token chunks over U{512..8192}-token prefixes),
+    served three ways: one pa_prefill call over the whole varlen batch; the
+    decode rows through pa_decode and the chunks through pa_prefill, back to
+    back on one stream; and the same two calls on two streams at once (the
+    decode on a second stream joined with events).  Medians of HIP-event times
+    on the first stream, after a sustained warm-up."""
+    c = wl.chunked_prefill_mixed()
+    dev = place(c)
+    pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+    nd = int((c.q_lens == 1).sum())
+    assert np.all(c.q_lens[:nd] == 1) and np.all(c.q_lens[nd:] > 1)
+    out = torch.empty((c.total_q_rows, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws_all = pa.alloc_prefill_workspace(c.batch, c.total_q_rows, c.max_q_len, c.num_q_heads,
+                                        c.num_kv_heads, c.max_blocks_per_seq)
+    q_dec, out_dec = dev.q[:nd], out[:nd]
+    tab_dec, len_dec = dev.block_table[:nd], dev.context_lens[:nd]
+    ws_dec = pa.alloc_decode_workspace(nd, c.num_q_heads, c.num_kv_heads)
+    q_chk, out_chk = dev.q[nd:], out[nd:]
+    tab_chk, len_chk = dev.block_table[nd:].contiguous(), dev.context_lens[nd:].contiguous()
+    cu_chk = (dev.cu_q[nd:] - nd).contiguous()
+    max_dec = int(c.context_lens[:nd].max())
+    rows_chk = c.total_q_rows - nd
+    ws_chk = pa.alloc_prefill_workspace(c.batch - nd, rows_chk, c.max_q_len, c.num_q_heads,
+                                        c.num_kv_heads, c.max_blocks_per_seq)
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    ev_fork, ev_join = torch.cuda.Event(), torch.cuda.Event()
+
+    def one_call():
+        pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, c.max_q_len, dev.k_cache, dev.v_cache,
+                   dev.block_table, c.scale, ws_all)
+
+    def decode_rows(stream=None):
+        pa.decode(out_dec, q_dec, dev.k_cache, dev.v_cache, tab_dec, len_dec, max_dec, c.scale, ws_dec,
+                  stream=stream)
+
+    def chunks():
+        pa.prefill(out_chk, q_chk, cu_chk, len_chk, c.max_q_len, dev.k_cache, dev.v_cache, tab_chk,
+                   c.scale, ws_chk)
+
+    def two_calls():
+        decode_rows()
+        chunks()
+
+    def two_streams():
+        ev_fork.record(s0)
+        s1.wait_event(ev_fork)
+        decode_rows(stream=s1)
+        chunks()
+        ev_join.record(s1)
+        s0.wait_event(ev_join)
+
+    def two_streams_prefill_first():
+        # the chunks' workgroups take the CUs first; the decode's fill the
+        # CUs their shorter blocks leave idle towards the end
+        ev_fork.record(s0)
+        chunks()
+        s1.wait_event(ev_fork)
+        decode_rows(stream=s1)
+        ev_join.record(s1)
+        s0.wait_event(ev_join)
+
+    res = {"workload": c.name, "decode_rows": nd, "chunk_rows": rows_chk}
+    for label, fn in (("one_pa_prefill_call", one_call), ("decode_then_prefill_one_stream", two_calls),
+                      ("decode_and_prefill_two_streams", two_streams),
+                      ("prefill_then_decode_two_streams", two_streams_prefill_first)):
+        _warm(fn, warmup)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(s0)
+            fn()
+            e1.record(s0)
+        torch.cuda.synchronize()
+        res[label + "_ms"] = round(float(np.median([a.elapsed_time(b) for a, b in evs])), 4)
+    fl = prefill_flops(c)
+    best = min(res["decode_then_prefill_one_stream_ms"], res["decode_and_prefill_two_streams_ms"],
+               res["prefill_then_decode_two_streams_ms"])
+    res["causal_gflop"] = round(fl / 1e9, 3)
+    res["best_TFLOPs"] = round(fl / (best * 1e-3) / 1e12, 1)
+    del dev, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_multi_report(name: str, steps: int, warmup: int) -> dict:
     """pa_decode_multi on a multi-query decode workload (several new tokens
     per sequence scored in one pass: the vector-ALU kernel up to 8 rows per
@@ -991,6 +1079,8 @@ def main(argv=None):
                      "long_prefix_chunk"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(30, args.steps // 5), 3)
+        print("[bench] extra chunked_prefill_mixed split by kernel", file=sys.stderr, flush=True)
+        extra["chunked_prefill_mixed_split"] = mixed_split_report(max(30, args.steps // 5), 3)
         for name in ("multi_query_decode", "spec_verify_decode"):
             print(f"[bench] extra {name} (pa_decode_multi)", file=sys.stderr, flush=True)
             extra[f"{name}_multi"] = decode_multi_report(name, max(20, args.steps // 5), 3)

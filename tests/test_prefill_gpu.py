@@ -82,6 +82,21 @@ def test_chunked_prefill_mixed_with_decode_rows():
     check(case, seqs_full=set(range(64)) | {64, 71}, heads_sampled=[0, 7, 12])
 
 
+def test_chunked_prefill_mixed_with_short_rows():
+    """One chunked-prefill call whose batch mixes rows with q_len 1 to 6 (decode
+    steps and speculative verification) with 512-token chunks over cached
+    prefixes; every short sequence and two chunks in full."""
+    rng = np.random.default_rng(48)
+    short = [1, 2, 3, 4, 5, 6] * 4
+    sctx = rng.integers(300, 3000, size=len(short)) + np.asarray(short)
+    prefix = rng.integers(256, 4096, size=4)
+    ctx = np.concatenate([sctx, prefix + 512])
+    ql = short + [512] * 4
+    case = wl.make_case("mixed_short_rows", "prefill", 48, ctx, 16, 8, q_lens=ql, rng=rng)
+    n = len(short)
+    check(case, seqs_full=set(range(n)) | {n, n + 3}, heads_sampled=[0, 9, 15])
+
+
 def test_multi_query_decode():
     """Speculative verification: 4 new tokens per sequence, causal among
     themselves, over U{512..4096} cached tokens."""
