@@ -296,8 +296,13 @@ size_t pa_prefill_workspace_size(int32_t batch, int64_t total_q_rows, int32_t ma
  *                   bytes (may be NULL when that is 0): scratch for the
  *                   partial states of query blocks whose context is split
  *                   across workgroups (a second kernel on the same stream
- *                   merges them).  No initial contents are needed.  Calls
- *                   that overlap in time must not share a workspace.
+ *                   merges them), and, when the query lengths are ragged
+ *                   (total_q_rows < batch * max_seqlen_q) and contexts may
+ *                   exceed 4 blocks, for the order in which the workgroups
+ *                   take the query blocks: longest first, written by a
+ *                   small kernel on the same stream before the attention
+ *                   kernel.  No initial contents are needed.  Calls that
+ *                   overlap in time must not share a workspace.
  *   Source: nano-vllm hub page, "Scheduler" (prefill fills the cache with the
  *   prompt); CSDN essay, reading vLLM's attention module (prefill kernel);
  *   the split-context merge follows the decode description in the same essay.

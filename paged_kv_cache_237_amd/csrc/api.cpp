@@ -156,9 +156,19 @@ size_t decode_ws_bytes(int32_t batch, int32_t num_kv_heads, int group, int64_t w
 // ~4 per slot the extra parts added merge traffic and prologues, and a
 // count that is not a multiple of the slots leaves some slots a second
 // workgroup while the rest idle.
+//
+// Longest-first plan: when the query lengths are ragged (total_q_rows below
+// batch * max_seqlen_q) the grid's blocks differ in length in ways only the
+// device sees (a chunked-prefill batch mixes one-token decode rows with long
+// chunks), and grid order can dispatch a long block after a round of short
+// ones.  A small kernel then sorts the items longest-first into the
+// workspace (plan_bytes) and the attention kernel takes them in that order.
+// Launches whose contexts fit 4 blocks (16 tiles per query block at most)
+// are left in grid order: no block is long enough to end the launch late.
 struct PrefillSplit {
   int split_tiles, max_splits, nqb_max;
-  size_t ml_bytes, o_bytes;
+  size_t ml_bytes, o_bytes, plan_bytes;
+  bool plan;
 };
 
 constexpr int64_t kPrefillSlots = 2 * 256;
@@ -208,13 +218,19 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
     if (best > 0.7 * one) want = 1;
   }
   ps.max_splits = int(std::min<int64_t>(want, cap));
+  // items of the plan (and workgroups of its 1-D grid, at most 2^24 of 256
+  // threads)
+  const int64_t items = int64_t(batch) * ps.max_splits * ps.nqb_max;
+  ps.plan = total_q_rows < int64_t(batch) * max_seqlen_q && max_blocks_per_seq > 4 &&
+            items * num_kv_heads < (int64_t(1) << 24);
+  ps.plan_bytes = ps.plan ? (size_t(pa::kPlanHeader + items) * sizeof(int32_t) + 255) & ~size_t(255) : 0;
   if (ps.max_splits == 1) {
     ps.ml_bytes = ps.o_bytes = 0;
     return ps;
   }
   const size_t rows = size_t(ps.max_splits) * size_t(std::max<int64_t>(total_q_rows, 0)) * size_t(num_q_heads);
   ps.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
-  ps.o_bytes = rows * size_t(pa::kDim) * sizeof(float);
+  ps.o_bytes = (rows * size_t(pa::kDim) * sizeof(float) + 255) & ~size_t(255);
   return ps;
 }
 
@@ -639,7 +655,7 @@ size_t pa_prefill_workspace_size(int32_t batch, int64_t total_q_rows, int32_t ma
     if (check_geometry(num_q_heads, num_kv_heads, head_dim, block_size, &group) != PA_OK) return 0;
     const PrefillSplit ps = prefill_split(batch, total_q_rows, max_seqlen_q, num_q_heads,
                                           num_kv_heads, group, max_blocks_per_seq);
-    return ps.ml_bytes + ps.o_bytes;
+    return ps.ml_bytes + ps.o_bytes + ps.plan_bytes;
   } catch (...) {
     return 0;
   }
@@ -667,7 +683,7 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
       return fail(PA_ERR_NULL_PTR, "pa_prefill: a pointer argument is NULL");
     const PrefillSplit ps = prefill_split(batch, total_q_rows, max_seqlen_q, num_q_heads,
                                           num_kv_heads, group, max_blocks_per_seq);
-    const size_t need = ps.ml_bytes + ps.o_bytes;
+    const size_t need = ps.ml_bytes + ps.o_bytes + ps.plan_bytes;
     if (need > 0) {
       if (workspace == nullptr) return fail(PA_ERR_WORKSPACE, "workspace is NULL");
       if (!aligned(workspace, 256)) return fail(PA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -700,8 +716,9 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
     a.max_splits = ps.max_splits;
     a.total_q = total_q_rows;
     char* wsb = static_cast<char*>(workspace);
-    a.rec_ml = need > 0 ? reinterpret_cast<float*>(wsb) : nullptr;
-    a.rec_o = need > 0 ? reinterpret_cast<float*>(wsb + ps.ml_bytes) : nullptr;
+    a.rec_ml = ps.ml_bytes > 0 ? reinterpret_cast<float*>(wsb) : nullptr;
+    a.rec_o = ps.o_bytes > 0 ? reinterpret_cast<float*>(wsb + ps.ml_bytes) : nullptr;
+    a.plan = ps.plan ? reinterpret_cast<int32_t*>(wsb + ps.ml_bytes + ps.o_bytes) : nullptr;
     if (debug_checks_on()) {
       pa::SeqCheckArgs c{};
       c.ctx_lens = context_lens;

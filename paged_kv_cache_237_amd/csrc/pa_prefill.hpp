@@ -32,10 +32,17 @@ struct PrefillArgs {
   int64_t total_q;   // rows the records are sized for
   float* rec_ml;     // [max_splits][total_q][hq][2] (m, l)
   float* rec_o;      // [max_splits][total_q][hq][kDim] unnormalised outputs
+  // Longest-first dispatch (null: grid order).  plan[0] = number of
+  // workgroup items n; plan[kPlanHeader + k], k < n, = the k-th longest
+  // (sequence, part, query block) as jrev * batch * max_splits + b *
+  // max_splits + part.  Written by the plan kernel on the same stream.
+  int32_t* plan;
 };
 
 // Query rows per prefill workgroup.
 constexpr int kPrefillRows = 128;
+// int32 words before the plan's item list (the count, padded to 256 B).
+constexpr int kPlanHeader = 64;
 
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t s);
 

@@ -273,10 +273,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   PrefillLds& sm = *reinterpret_cast<PrefillLds*>(lds_raw);
   float (*rowf)[32] = sm.rowf;
 
-  const int b = blockIdx.x / a.max_splits;
-  const int part = blockIdx.x - b * a.max_splits;
-  const int g = blockIdx.y;
-  const int jrev = blockIdx.z;
+  int b, part, g, jrev;
+  if (a.plan != nullptr) {
+    // 1-D grid: item k of the longest-first list, kv head fastest
+    const int k = int(blockIdx.x) / a.hkv;
+    g = int(blockIdx.x) - k * a.hkv;
+    if (k >= a.plan[0]) return;
+    const int id = a.plan[kPlanHeader + k];
+    const int nx = a.batch * a.max_splits;
+    jrev = id / nx;
+    const int x = id - jrev * nx;
+    b = x / a.max_splits;
+    part = x - b * a.max_splits;
+  } else {
+    b = int(blockIdx.x) / a.max_splits;
+    part = int(blockIdx.x) - b * a.max_splits;
+    g = blockIdx.y;
+    jrev = blockIdx.z;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -515,6 +529,83 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Longest-first order of the workgroup items (sequence, part, query block)
+// of a launch whose blocks differ in length on the device (ragged query
+// lengths): the hardware dispatches workgroups in grid order as slots free
+// up, so a long block dispatched after the first round of short ones ends
+// the launch late.  One workgroup counts the items per length (tiles of
+// their part, lengths of kPlanBuckets - 1 tiles and more counted together),
+// turns the counts into offsets in order of decreasing length, and writes
+// every item at its offset; items of one length keep no particular order
+// (each writes its own rows, so the outputs do not depend on it).
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 4096;
+
+template <int G>
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a) {
+  constexpr int QB = kRowsPerWG / G;
+  __shared__ int cnt[kPlanBuckets];  // per key = kPlanBuckets - 1 - min(length, kPlanBuckets - 1)
+  __shared__ int wsum[kPlanThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kPlanBuckets; i += kPlanThreads) cnt[i] = 0;
+  __syncthreads();
+
+  const int nqb_max = (a.max_q + QB - 1) / QB;
+  const int64_t cands = int64_t(a.batch) * nqb_max;
+  const int nx = a.batch * a.max_splits;
+  // fn(item id, key) for every item of the launch
+  auto for_items = [&](auto&& fn) {
+    for (int64_t c = tid; c < cands; c += kPlanThreads) {
+      const int b = int(c / nqb_max);
+      const int jrev = int(c - int64_t(b) * nqb_max);
+      const BlockGeom<G> bg(a, b, jrev);
+      if (jrev >= bg.nqb) continue;
+      for (int part = 0; part < bg.nsplit; ++part) {
+        const int len = int(int64_t(bg.ntiles) * (part + 1) / bg.nsplit) -
+                        int(int64_t(bg.ntiles) * part / bg.nsplit);
+        fn(jrev * nx + b * a.max_splits + part, kPlanBuckets - 1 - min(len, kPlanBuckets - 1));
+      }
+    }
+  };
+  for_items([&](int, int key) { atomicAdd(&cnt[key], 1); });
+  __syncthreads();
+
+  // exclusive scan of the counts in key order: thread t owns keys 4t .. 4t+3
+  constexpr int kPer = kPlanBuckets / kPlanThreads;
+  int c4[kPer], own = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    c4[i] = cnt[kPer * tid + i];
+    own += c4[i];
+  }
+  int incl = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanThreads / 64; ++i) {
+    before += i < w ? wsum[i] : 0;
+    total += wsum[i];
+  }
+  int off = before + incl - own;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cnt[kPer * tid + i] = off;
+    off += c4[i];
+  }
+  if (tid == 0) a.plan[0] = total;
+  __syncthreads();
+
+  int32_t* order = a.plan + kPlanHeader;
+  for_items([&](int id, int key) { order[atomicAdd(&cnt[key], 1)] = id; });
+}
+
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
   constexpr int QB = kRowsPerWG / G;
@@ -524,8 +615,17 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
       int(kPrefillLds));
   if (attr != hipSuccess) return attr;
   const int nqb = (a.max_q + QB - 1) / QB;
-  const dim3 grid(unsigned(a.batch) * unsigned(a.max_splits), unsigned(a.hkv), unsigned(nqb));
-  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), kPrefillLds, s, a);
+  if (a.plan != nullptr) {
+    hipLaunchKernelGGL(prefill_plan_kernel<G>, dim3(1), dim3(kPlanThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // as many workgroups as the grid below holds; those past the count exit
+    const unsigned n = unsigned(a.batch) * unsigned(a.max_splits) * unsigned(nqb) * unsigned(a.hkv);
+    hipLaunchKernelGGL(prefill_kernel<G>, dim3(n), dim3(256), kPrefillLds, s, a);
+  } else {
+    const dim3 grid(unsigned(a.batch) * unsigned(a.max_splits), unsigned(a.hkv), unsigned(nqb));
+    hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), kPrefillLds, s, a);
+  }
   if (a.max_splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
