@@ -110,8 +110,7 @@ def read_ceiling(sizes, labels, steps: int = 30) -> dict:
                 if st != 0:
                     raise RuntimeError(f"pa_probe_stream_read returned {st}")
             _warm(call, 20)
-            _, ts = _events_ms(call, steps)
-            ms = float(np.median(ts))
+            ms = _events_batch_ms(call, steps)
             res[label + ("_nt" if nt else "")] = {"bytes": n, "us": round(ms * 1e3, 2),
                                                   "GBps": round(n / (ms * 1e-3) / 1e9, 1)}
     del buf, sink
@@ -175,6 +174,23 @@ def _events_ms(fn, steps, before=None):
     return float(np.mean(ts)), ts
 
 
+def _events_batch_ms(fn, steps):
+    """Mean time (ms) of one call of fn from a pair of HIP events around
+    `steps` calls launched back to back on the stream the kernels run on: the
+    kernels' own duration plus the few-microsecond gap between two kernels of
+    one stream, without the host's launch latency that events around a single
+    call also catch."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(torch.cuda.current_stream())
+    for _ in range(steps):
+        fn()
+    b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True) -> dict:
     """Times `steps` decode steps after `warmup`.  A step stores each
     sequence's new token and attends over the whole context; it runs as one
@@ -185,8 +201,9 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True)
     a HIP graph and replayed ("*_graph_ms"; each replay of a graph this small
     adds a few microseconds of its own).  graph=False skips the graph
     timings.  Kernel
-    times ("append_ms", "decode_ms", "store_ms") are HIP events around single
-    eager calls on the stream the kernels run on; "decode_ms_flushed" are
+    times ("append_ms", "decode_ms", "store_ms") are HIP events around
+    `steps` eager calls launched back to back on the stream the kernels run
+    on, divided by `steps`; "decode_ms_flushed" are
     pa_decode times with the caches (4 MB L2 per XCD, 256 MB MALL) flushed
     before each call by reading 1 GiB of other data, outside the events: what
     one layer of a deep model sees, since its cache is read again only after
@@ -219,9 +236,9 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True)
         two_calls()
         append()
     res = {}
-    res["append_ms"], _ = _events_ms(append, steps)
-    res["store_ms"], _ = _events_ms(store, steps)
-    res["decode_ms"], _ = _events_ms(decode, steps)
+    res["append_ms"] = _events_batch_ms(append, steps)
+    res["store_ms"] = _events_batch_ms(store, steps)
+    res["decode_ms"] = _events_batch_ms(decode, steps)
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     _, res["decode_ms_flushed"] = _events_ms(decode, steps,
@@ -441,29 +458,20 @@ def decode_multi_report(name: str, steps: int, warmup: int) -> dict:
     per sequence scored in one pass: the vector-ALU kernel up to 8 rows per
     (sequence, kv head), the matrix-core kernel for 9 to 32): the algorithmic
     bytes (every context's K/V rows once, q in, out written, table entries,
-    lengths) over the HBM peak, HIP events around single launches."""
+    lengths) over the HBM peak, HIP events around back-to-back launches."""
     c = wl.CONFIGS[name]()
     ql = int(c.q_lens[0])
     dev = place(c)
     pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
     out = torch.empty((c.total_q_rows, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device="cuda")
     ws = pa.alloc_decode_multi_workspace(c.batch, ql, c.num_q_heads, c.num_kv_heads)
-    stream = torch.cuda.current_stream()
 
     def call():
         pa.decode_multi(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens, ql,
                         c.max_context_len, c.scale, ws)
 
     _warm(call, warmup)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record(stream)
-        call()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    ms = _events_batch_ms(call, steps)
     kvb = int(c.context_lens.sum()) * c.num_kv_heads * c.head_dim * 2 * 2
     blocks = sum(wl.blocks_for(int(n)) for n in c.context_lens)
     alg = kvb + 2 * c.total_q_rows * c.num_q_heads * c.head_dim * 2 + 4 * blocks + 4 * c.batch
@@ -572,7 +580,20 @@ def block_manager_report(steps: int = 512) -> dict:
 # Profile summaries (rocprofv3 CSV -> short text/JSON under profiles/)
 
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", "decode.hip")
+# each kernel's source and the headers it includes; the digests below add the
+# hipcc options it is compiled with
+_CSRC = os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc")
+DECODE_SRC = tuple(os.path.join(_CSRC, f) for f in (
+    "decode.hip", "decode_common.hpp", "pa_device.hpp", "pa_internal.hpp", "pa_common.hpp"))
+
+
+def kernel_digest(paths, source_name: str) -> str:
+    """Digest of what a kernel's code depends on: its source, the headers it
+    includes and the hipcc options of its translation unit."""
+    import hashlib
+    from paged_kv_cache_237_amd import build as b
+    flags = json.dumps([b.HIPCC_FLAGS, b.SOURCE_FLAGS.get(source_name, [])]).encode()
+    return hashlib.sha256(source_digest(*paths).encode() + flags).hexdigest()[:16]
 
 
 def source_digest(*paths: str) -> str:
@@ -621,7 +642,7 @@ def _pmc_per_kernel(counter_csv: str, counter: str):
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key: str,
-                      out_json: str, commands, source: str = DECODE_SRC) -> dict:
+                      out_json: str, commands, source=DECODE_SRC) -> dict:
     """HBM bytes per launch of the kernel whose name contains kernel_key, from
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the value the
     same counter reads for a plain device copy of copy_mib MiB."""
@@ -637,15 +658,17 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key:
         return k, (sum(v) / len(v), len(v))
 
     def pick_copy(d):
-        """The single largest copy dispatch: the copy of known size."""
+        """The largest dispatch of the runtime's device copy: the copy of
+        known size (torch's elementwise kernels are not candidates: the ones
+        that fill the input pools write more than the probe copy)."""
         best = None
         for k, v in d.items():
-            if "copyBuffer" in k or "elementwise_kernel" in k:
+            if "copyBuffer" in k:
                 m = max(v)
                 if best is None or m > best[1][0]:
                     best = (k, (m, 1))
         if best is None:
-            raise SystemExit("no copy kernel in the counter CSV")
+            raise SystemExit("no device copy dispatch in the counter CSV")
         return best
 
     known = copy_mib * 2**20
@@ -666,10 +689,10 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernel_key:
         "commands": list(commands),
     }
     if source == DECODE_SRC:
-        res["decode_source_sha256_16"] = source_digest(DECODE_SRC)
+        res["decode_source_sha256_16"] = kernel_digest(DECODE_SRC, "decode.hip")
     else:
-        res["source"] = os.path.relpath(source, ROOT)
-        res["source_sha256_16"] = source_digest(source)
+        res["source"] = os.path.relpath(source[0], ROOT)
+        res["source_sha256_16"] = kernel_digest(source, os.path.basename(source[0]))
     json.dump(res, open(out_json, "w"), indent=1)
     return res
 
@@ -682,12 +705,8 @@ PREFILL_COUNTERS = os.path.join(PROFILES, "prefill_8x2048_sq_counters.json")
 
 
 def prefill_digest() -> str:
-    """Digest of what the prefill kernel's code depends on: its source, the
-    headers it includes and the hipcc options it is compiled with."""
-    import hashlib
-    from paged_kv_cache_237_amd import build as b
-    flags = json.dumps([b.HIPCC_FLAGS, b.SOURCE_FLAGS.get("prefill.hip", [])]).encode()
-    return hashlib.sha256(source_digest(*PREFILL_SRC).encode() + flags).hexdigest()[:16]
+    """Digest of what the prefill kernel's code depends on."""
+    return kernel_digest(PREFILL_SRC, "prefill.hip")
 
 
 def summarize_counters(out_md: str, kernel_key: str, csvs, commands) -> dict:
@@ -750,7 +769,8 @@ def recorded_prefill_counters():
     return rec.get("ratios")
 
 
-STORE_SRC = os.path.join(ROOT, "paged_kv_cache_237_amd", "csrc", "store_kv.hip")
+STORE_SRC = tuple(os.path.join(_CSRC, f) for f in (
+    "store_kv.hip", "pa_device.hpp", "pa_internal.hpp", "pa_common.hpp"))
 STORE_TRAFFIC = os.path.join(PROFILES, "store_16384_tokens_traffic.json")
 
 
@@ -760,7 +780,7 @@ def recorded_store_traffic():
     if not os.path.exists(STORE_TRAFFIC):
         return None
     rec = json.load(open(STORE_TRAFFIC))
-    if rec.get("source_sha256_16") != source_digest(STORE_SRC):
+    if rec.get("source_sha256_16") != kernel_digest(STORE_SRC, "store_kv.hip"):
         return None
     return int(round(rec["traffic_bytes"]))
 
@@ -772,7 +792,7 @@ def recorded_traffic(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("decode_source_sha256_16") != source_digest(DECODE_SRC):
+    if rec.get("decode_source_sha256_16") != kernel_digest(DECODE_SRC, "decode.hip"):
         return None
     return int(round(rec["traffic_bytes"]))
 
@@ -994,8 +1014,8 @@ def main(argv=None):
     ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
                     help="OUT_MD KERNEL_KEY CSV [CSV ...]: write a summary of SQ/GRBM counter "
                          "CSVs of one kernel (rocprofv3 --pmc passes) and exit")
-    ap.add_argument("--traffic-source", default=DECODE_SRC,
-                    help="kernel source whose digest a traffic summary records (default: decode)")
+    ap.add_argument("--traffic-source", choices=("decode", "store"), default="decode",
+                    help="kernel whose source digest a traffic summary records (default: decode)")
     ap.add_argument("--commands", nargs="*", default=[],
                     help="the profiler commands recorded in a traffic summary")
     args = ap.parse_args(argv)
@@ -1004,8 +1024,8 @@ def main(argv=None):
         return 0
     if args.summarize_traffic:
         f, w, mib, key, out = args.summarize_traffic
-        print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands,
-                                           os.path.abspath(args.traffic_source))))
+        src = DECODE_SRC if args.traffic_source == "decode" else STORE_SRC
+        print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands, src)))
         return 0
     if args.summarize_counters:
         out_md, key, *csvs = args.summarize_counters

@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "pa_internal.hpp"
+#include "pa_prefill.hpp"
 
 namespace {
 

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "pa_internal.hpp"
+#include "pa_prefill.hpp"
 
 namespace pa {
 

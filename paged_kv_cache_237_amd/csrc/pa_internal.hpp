@@ -10,7 +10,6 @@
 #include <string>
 
 #include "pa_common.hpp"
-#include "pa_prefill.hpp"
 
 namespace pa {
 
