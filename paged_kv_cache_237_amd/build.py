@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libpa.so")
 # out of libpa so that the library exports only the pa_* interface
 PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
 
-SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "blocks.hip",
+SOURCES = ["api.cpp", "store_kv.hip", "decode.hip", "decode_mfma.hip", "decode_mfma16.hip", "prefill.hip", "blocks.hip",
            "block_manager.cpp", "checks.hip"]
 PROBE_SOURCES = ["read_ceiling.hip"]
 

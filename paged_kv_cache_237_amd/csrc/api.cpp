@@ -237,13 +237,16 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
 
 // Virtual heads per (sequence, kv head) of a decode of q_per_seq rows: group
 // * q_per_seq rounded up to a power of two when that is at most 8 (the
-// vector-ALU kernel), 32 for 9 to 32 rows (the matrix-core kernel), 0 beyond.
+// vector-ALU kernel), 16 for 9 to 16 rows and 32 for 17 to 32 (the
+// matrix-core kernels), 0 beyond.
 constexpr int kMfmaRows = 32;
+constexpr int kMfma16Rows = 16;
 int virtual_group(int group, int32_t q_per_seq) {
   if (q_per_seq < 1 || q_per_seq > kMfmaRows) return 0;
   const int rows = group * q_per_seq;
   if (rows > kMfmaRows) return 0;
-  if (rows > 8) return kMfmaRows;
+  if (rows > kMfma16Rows) return kMfmaRows;
+  if (rows > 8) return kMfma16Rows;
   int gv = 1;
   while (gv < rows) gv *= 2;
   return gv;
@@ -354,8 +357,10 @@ int decode_rows(void* out, const void* q, const void* k_new, const void* v_new, 
       if (ce != hipSuccess) return hip_fail(ce, "decode checks");
       if (flags) return precondition_fail(flags);
     }
-    const hipError_t e = gv == kMfmaRows ? pa::launch_decode_mfma(a, static_cast<hipStream_t>(stream))
-                                         : pa::launch_decode(a, gv, static_cast<hipStream_t>(stream));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = gv == kMfmaRows     ? pa::launch_decode_mfma(a, st)
+                         : gv == kMfma16Rows ? pa::launch_decode_mfma16(a, st)
+                                             : pa::launch_decode(a, gv, st);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
   } catch (...) {

@@ -40,19 +40,15 @@
 // decode, the kernel is bound by HBM bandwidth.
 #include <math.h>
 
-#include "decode_common.hpp"
+#include "decode_mfma_common.hpp"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kMfRows = 32;       // rows per segment: one MFMA block
 constexpr int kMfWaves = 4;       // waves per workgroup, one per SIMD
-constexpr int kMfVtStride = 72;   // bf16 per transposed-V row in LDS (64 keys + pad)
-constexpr float kMfLazy = 8.f;    // log2 headroom before O is rescaled
-constexpr uint32_t kMfOnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 // Tiles whose K and V are in flight while one is computed: 1 (the next
 // tile's loads go into the registers the current tile frees) or 2 (two
 // register buffers, alternating).
@@ -66,41 +62,6 @@ struct MfLds {
   float rowf[kMfRows];
 };
 
-__device__ __forceinline__ bf16x8_t as_bf8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-__device__ __forceinline__ uint32_t word_at(const uint4& u, int i) {
-  return i == 0 ? u.x : (i == 1 ? u.y : (i == 2 ? u.z : u.w));
-}
-
-// Compiler-level ordering of one wave's LDS accesses (the hardware keeps a
-// wave's LDS operations in order; the transposed tile is written and read
-// through differently typed pointers).
-__device__ __forceinline__ void lds_order() {
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" ::: "memory");
-}
-
-struct MfTile {
-  __amdgpu_buffer_rsrc_t rk, rv;
-  int r0, valid;  // first row of the tile in its block; tokens inside the context
-};
-
-// Tile t of segment (sequence, kv head g) whose block-table entry is phys:
-// buffer descriptors whose ranges end at the block-head tile (K) and after
-// the last valid row (V), so rows past the context load zeros (the cache may
-// hold NaN patterns there).  A bad entry (or the "next tile" past a run's
-// end, phys = -1) gives no valid row.
-__device__ __forceinline__ MfTile mf_tile(const DecodeArgs& a, int phys, int g, int t, int ctx) {
-  MfTile tl;
-  const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
-  tl.valid = ok ? min(kTile, ctx - t * kTile) : 0;
-  tl.r0 = (t & 3) * kTile;
-  const int64_t bh = (ok ? int64_t(phys) : 0) * a.hkv + g;
-  tl.rk = make_rsrc(a.k_cache + bh * (kChunks * kBlock), 65536u);
-  tl.rv = make_rsrc(a.v_cache + bh * (kBlock * kChunks), uint32_t(tl.r0 + tl.valid) * 256u);
-  return tl;
-}
-
 // K as A operands: kr[8 ms + ks] = chunk 2 ks + half of token 32 ms + col.
 __device__ __forceinline__ void mf_issue_k(const MfTile& tl, uint4 (&kr)[16]) {
   const int lane = lane_id();
@@ -112,17 +73,6 @@ __device__ __forceinline__ void mf_issue_k(const MfTile& tl, uint4 (&kr)[16]) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kr[8 * ms + ks] = buf_load16_stream(tl.rk, off + uint32_t(ks) * 8192u, 0u);
   }
-}
-
-// V rows for the transposed store: vr[4 j + i] = chunk (lane & 15) of token
-// 4 kq + i, kq = (lane >> 4) + 4 j (16 lanes read one 256-byte row).
-__device__ __forceinline__ void mf_issue_v(const MfTile& tl, uint4 (&vr)[16]) {
-  const int lane = lane_id();
-  const uint32_t base = (uint32_t(tl.r0 + 4 * (lane >> 4)) * kChunks + uint32_t(lane & 15)) * 16u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vr[4 * j + i] = buf_load16_stream(tl.rv, base + uint32_t(16 * j + i) * 256u, 0u);
 }
 
 // The tile's V into LDS as [dim][key], each 16 keys in the order the P
@@ -234,38 +184,6 @@ __device__ void mf_merge(const DecodeArgs& a, int seg, int b, int g, int w0, int
     uint2* out = reinterpret_cast<uint2*>(a.out + vrow<kMfRows, true>(a, b, g, rh + r) * kDim + d0);
     *out = make_uint2(pack_bf16x2(U[r].x * inv, U[r].y * inv), pack_bf16x2(U[r].z * inv, U[r].w * inv));
   }
-}
-
-// A tile of the flattened list as a wave's stream sees it (wave-uniform):
-// its segment (b, g), index t of nt in the segment, the context, the block
-// holding it; live when it belongs to the run (and the batch).
-struct MfCur {
-  int b, g, t, nt, ctx, phys;
-  bool live;
-};
-
-// The tile after c: the next one of its segment or the first of the next
-// non-empty segment; live only when in_run (it is still inside the run).
-__device__ __forceinline__ MfCur mf_next(const DecodeArgs& a, const MfCur& c, bool in_run) {
-  MfCur n = c;
-  n.live = false;
-  n.phys = -1;
-  if (!c.live || !in_run) return n;
-  n.t = c.t + 1;
-  if (n.t == c.nt) {
-    n.t = 0;
-    if (++n.g == a.hkv) {
-      n.g = 0;
-      do {
-        n.b = __builtin_amdgcn_readfirstlane(n.b + 1);
-        n.ctx = n.b < a.batch ? clamp_ctx(a, ld_uniform(a.ctx_lens, n.b)) : 0;
-        n.nt = n.b < a.batch ? tiles_of(n.ctx) : 1;
-      } while (n.nt == 0);
-    }
-  }
-  n.live = n.b < a.batch;
-  if (n.live) n.phys = ld_uniform(a.block_table, int64_t(n.b) * a.mbps + (n.t >> 2));
-  return n;
 }
 
 // Streams tiles [pos, end) of the flattened list (this wave's run) with two

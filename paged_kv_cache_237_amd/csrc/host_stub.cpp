@@ -18,6 +18,7 @@ hipError_t launch_store_kv(const StoreArgs&, hipStream_t) { return hipErrorNoDev
 hipError_t launch_copy_blocks(const CopyBlocksArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(const DecodeArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_decode_mfma16(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefill(const PrefillArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t noalloc_scratch(hipStream_t, void**) { return hipErrorNoDevice; }
 

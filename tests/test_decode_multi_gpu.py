@@ -52,7 +52,8 @@ def test_multi_query_decode_workload():
 
 @pytest.mark.parametrize("hq,hkv,ql", [(8, 8, 8), (8, 8, 3), (8, 8, 1), (16, 8, 4), (16, 8, 3),
                                        (16, 8, 2), (32, 8, 2), (64, 8, 1), (4, 1, 2),
-                                       # 9..32 rows per (sequence, kv head): the matrix-core kernel
+                                       # 9..16 and 17..32 rows per (sequence, kv head): the
+                                       # matrix-core kernels
                                        (16, 8, 5), (16, 8, 6), (32, 8, 5), (32, 8, 6), (32, 8, 3),
                                        (32, 8, 8), (64, 8, 4), (64, 8, 2), (8, 8, 9), (8, 8, 32),
                                        (4, 1, 8)])
@@ -93,7 +94,7 @@ def test_decode_multi_matches_prefill():
 def test_speculative_verification_workload():
     """64 sequences each verify 5 drafted tokens plus the next one (6 rows)
     over U{512..4096} cached tokens: 12 rows per (sequence, kv head), the
-    matrix-core kernel."""
+    16-row matrix-core kernel."""
     check(wl.spec_verify_decode(), 6)
 
 
@@ -114,17 +115,19 @@ def test_decode_multi_many_rows_matches_prefill(hq):
     assert np.abs(multi - pre).max() <= 1.5e-2
 
 
-def test_decode_multi_long_contexts_cut_across_waves():
-    """Few long sequences with 6 rows at 32 q / 8 kv heads: every segment is
-    cut into many runs and merged from 32-row partial records (sampled
-    sequences against the oracle)."""
-    case = wl.make_case("multi_long", "prefill", 88, [40000, 70001, 6, 9000], 32, 8, q_lens=[6] * 4)
+@pytest.mark.parametrize("hq", [16, 32])
+def test_decode_multi_long_contexts_cut_across_waves(hq):
+    """Few long sequences with 6 rows at 16 or 32 q / 8 kv heads (12 or 24
+    rows per kv head: the 16-row and the 32-row matrix-core kernel): every
+    segment is cut into many runs and merged from partial records."""
+    case = wl.make_case(f"multi_long_{hq}", "prefill", 88, [40000, 70001, 6, 9000], hq, 8, q_lens=[6] * 4)
     check(case, 6)
 
 
 def test_decode_multi_negative_scale():
-    """A negative logit scale (allowed: finite) on both decode-multi kernels."""
-    for hq, ql in ((16, 2), (32, 6)):
+    """A negative logit scale (allowed: finite) on the three decode-multi
+    kernels (4, 12 and 24 rows per kv head)."""
+    for hq, ql in ((16, 2), (16, 6), (32, 6)):
         case = wl.make_case(f"multi_negscale_{hq}", "prefill", 90 + hq, [ql, 70, 700, 3000], hq, 8,
                             q_lens=[ql] * 4, scale=-0.09)
         check(case, ql)

@@ -77,8 +77,8 @@ def test_split_plans_agree_with_oracle_and_ignore_placement(hq, append):
 @pytest.mark.parametrize("hq,ql", [(16, 6), (32, 5)])
 def test_multi_row_split_plans(hq, ql):
     """pa_decode_multi with 12 or 20 rows per (sequence, kv head) -- the
-    matrix-core kernel, whose partial records hold 32 rows -- under the same
-    plans, against the oracle's causal attention."""
+    matrix-core kernels, whose partial records hold 16 and 32 rows -- under
+    the same plans, against the oracle's causal attention."""
     case = wl.make_case(f"plans_multi_{hq}", "prefill", 140 + hq, [ql, 63 + ql, 700, 3000, 4096, 257],
                         hq, 8, q_lens=[ql] * 6, num_blocks=40)
     dev = place(case)
