@@ -455,8 +455,8 @@ def mixed_split_report(steps: int, warmup: int) -> dict:
 
 def decode_multi_report(name: str, steps: int, warmup: int) -> dict:
     """pa_decode_multi on a multi-query decode workload (several new tokens
-    per sequence scored in one pass: the vector-ALU kernel up to 8 rows per
-    (sequence, kv head), the matrix-core kernels for 9 to 16 and 17 to 32):
+    per sequence scored in one pass: the vector-ALU kernel up to 4 rows per
+    (sequence, kv head), the matrix-core kernels for 5 to 16 and 17 to 32):
     the algorithmic
     bytes (every context's K/V rows once, q in, out written, table entries,
     lengths) over the HBM peak, HIP events around back-to-back launches."""
@@ -479,7 +479,7 @@ def decode_multi_report(name: str, steps: int, warmup: int) -> dict:
     gbs = alg / (ms * 1e-3) / 1e9
     rows = ql * c.num_q_heads // c.num_kv_heads
     kernel = ("decode_mfma_kernel" if rows > 16 else
-              "decode_mfma16_kernel" if rows > 8 else "decode_split_kernel (several rows)")
+              "decode_mfma16_kernel" if rows > 4 else "decode_split_kernel (several rows)")
     del dev, out, ws
     torch.cuda.empty_cache()
     return {"workload": c.name, "entry_point": "pa_decode_multi", "q_per_seq": ql,

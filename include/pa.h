@@ -244,11 +244,11 @@ int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const 
  *                   b * q_per_seq + i, 16-B aligned.
  *   q_per_seq     : 1 .. 32, with q_per_seq * num_q_heads / num_kv_heads <= 32
  *                   (else PA_ERR_UNSUPPORTED): the rows of one (sequence, kv
- *                   head) are processed together -- up to 8 like the query
- *                   heads of one kv head in pa_decode, 9 to 16 as one
- *                   block of 16 rows and 17 to 32 as one block of 32 rows
- *                   on the matrix cores (P rounded to bf16 before P.V, as in
- *                   pa_prefill).
+ *                   head) are processed together -- up to 4 like the query
+ *                   heads of one kv head in pa_decode (q_per_seq = 1: up to
+ *                   8), 5 to 16 as one block of 16 rows and 17 to 32 as one
+ *                   block of 32 rows on the matrix cores (P rounded to bf16
+ *                   before P.V, as in pa_prefill).
  *   context_lens  : int32 [batch], each >= q_per_seq for meaningful rows (a
  *                   row whose position is negative sees no key and is zero).
  *   workspace     : >= pa_decode_multi_workspace_size(...) bytes; same rules

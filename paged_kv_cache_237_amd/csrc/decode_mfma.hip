@@ -6,7 +6,7 @@
 // first and third sections: paged cache, exact attention in on-chip tiles;
 // its section on speculative decoding: a draft model proposes a few tokens
 // and the target model checks them in one pass) -- when the rows of one
-// (sequence, kv head), q_per_seq tokens x G query heads, number 9 to 32: too
+// (sequence, kv head), q_per_seq tokens x G query heads, number 17 to 32: too
 // many for the vector-ALU decode kernel (decode.hip), which keeps a row's
 // accumulators per head in registers.
 //

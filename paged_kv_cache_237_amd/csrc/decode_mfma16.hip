@@ -1,6 +1,7 @@
-// Decode of 9 to 16 query rows per (sequence, kv head) on the matrix cores
+// Decode of 5 to 16 query rows per (sequence, kv head) on the matrix cores
 // (gfx950): pa_decode_multi for, e.g., 5 drafted tokens + the next one at 2 q
-// heads per kv head (12 rows).
+// heads per kv head (12 rows), or 4 new tokens at 2 (8 rows; up to 8 rows of
+// several tokens the vector-ALU decode measured 16-20 % slower).
 //
 // What it computes is decode_mfma.hip's (CSDN essay comparing nanoVLLM and
 // vLLM, first and third sections: paged cache, exact attention in on-chip

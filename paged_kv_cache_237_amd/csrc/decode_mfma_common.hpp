@@ -1,6 +1,6 @@
 // Pieces shared by the matrix-core decode kernels (decode_mfma.hip: 17..32
 // rows per (sequence, kv head) on v_mfma_f32_32x32x16_bf16;
-// decode_mfma16.hip: 9..16 rows on v_mfma_f32_16x16x32_bf16): a tile's
+// decode_mfma16.hip: 5..16 rows on v_mfma_f32_16x16x32_bf16): a tile's
 // buffer descriptors, the V loads for the transposed LDS store, and the walk
 // of a wave's run over the flattened tile list.  Both kernels read K and V in
 // 64-token tiles with the non-temporal policy and keep V transposed in LDS.

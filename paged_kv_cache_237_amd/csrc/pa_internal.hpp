@@ -85,7 +85,7 @@ constexpr int kDecodeWavesPerCU = 8;
 // their waves get runs 11/12 as long and all XCDs finish together.
 constexpr int kRunWeightEven = 12;
 constexpr int kRunWeightOdd = 11;
-// The matrix-core decodes of 9..16 and 17..32 rows per (sequence, kv head)
+// The matrix-core decodes of 5..16 and 17..32 rows per (sequence, kv head)
 // (decode_mfma16.hip, "G" = 16; decode_mfma.hip, "G" = 32) run 4 waves per
 // CU, one per SIMD.
 __host__ __device__ constexpr int decode_group_waves(int g) { return g >= 8 ? 4 : 8; }
@@ -121,7 +121,7 @@ hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t s);
 // pa_decode_multi with 17 to 32 rows per (sequence, kv head), on the matrix
 // cores (records of 32 rows).
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
-// ... with 9 to 16 rows (records of 16 rows).
+// ... with 5 to 16 rows (records of 16 rows).
 hipError_t launch_decode_mfma16(const DecodeArgs& a, hipStream_t s);
 
 // Library-owned decode workspace of the allocation-free decode step: the

@@ -50,10 +50,11 @@ def test_multi_query_decode_workload():
     check(wl.multi_query_decode(), 4)
 
 
+# rows per (sequence, kv head) = hq / hkv * ql: up to 4 (and 8 of one token)
+# on the vector-ALU kernel, 5..16 of several tokens on the 16-row and 17..32
+# on the 32-row matrix-core kernel
 @pytest.mark.parametrize("hq,hkv,ql", [(8, 8, 8), (8, 8, 3), (8, 8, 1), (16, 8, 4), (16, 8, 3),
                                        (16, 8, 2), (32, 8, 2), (64, 8, 1), (4, 1, 2),
-                                       # 9..16 and 17..32 rows per (sequence, kv head): the
-                                       # matrix-core kernels
                                        (16, 8, 5), (16, 8, 6), (32, 8, 5), (32, 8, 6), (32, 8, 3),
                                        (32, 8, 8), (64, 8, 4), (64, 8, 2), (8, 8, 9), (8, 8, 32),
                                        (4, 1, 8)])
