@@ -19,11 +19,13 @@
 //   O  = P V    : A = bf16(P) taken straight from the S^T accumulator -- the
 //                 contraction runs over keys in the accumulator's register
 //                 order (per 16 keys, lane half h holds keys 4h..4h+3 and
-//                 8+4h..8+4h+3), and V is kept in LDS transposed ([dim][key])
-//                 with each 16 keys stored in the order 0-3, 8-11, 4-7,
-//                 12-15, so a lane's 8 keys of one MFMA are one 16-byte read
-//                 and P never moves between lanes.  The transposed tile is
-//                 written with 8-byte stores (4 keys of one dim each).
+//                 8+4h..8+4h+3), so P never moves between lanes.  V is kept
+//                 in LDS as it is in the cache ([key][dim], one 16-byte store
+//                 per chunk), and a lane's B operand -- its dim of those 8
+//                 keys -- is gathered by two transposing LDS reads
+//                 (ds_read_b64_tr_b16: in each 16-lane group, lane j points
+//                 at 4 dims of key j / 4 and receives dim j % 4 of the
+//                 group's 4 keys, so the group holds 16 dims x 4 keys).
 // Online softmax in the log2 domain (scale*log2 e folded into one FMA) with a
 // lazy rescale: the reference max only moves when a row's max grows by more
 // than 2^8, so O is rescaled rarely.  Tiles entirely above a wave's diagonal
@@ -51,19 +53,21 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerWG = kPrefillRows;  // query rows (head, position) per workgroup: 32 per wave
 constexpr int kKeys = 64;        // keys per K/V tile
-constexpr int kVtStride = 72;    // bf16 per transposed-V row in LDS (64 keys + pad, 16-B aligned)
+constexpr int kVStride = 160;    // bf16 per V row (one key) in LDS: 128 dims + pad, 320 B
 constexpr float kLazyRescale = 8.f;  // log2 headroom before O is rescaled
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
-// LDS: two K tiles and two transposed V tiles; tile t is read from buffer t&1
-// while tile t+1 waits in registers.
+// LDS: two K tiles and two V tiles; tile t is read from buffer t&1 while
+// tile t+1 waits in registers.
 struct __align__(16) PrefillLds {
-  uint4 k[2][kChunks * kKeys];        // [buf][chunk][key] 16-byte chunks: 2 x 16 KiB
-  uint16_t vt[2][kDim * kVtStride];   // [buf][dim][key] bf16: 2 x 17 KiB
-  float rowf[4][32];                  // per-wave row factors
+  uint4 k[2][kChunks * kKeys];       // [buf][chunk][key] 16-byte chunks: 2 x 16 KiB
+  uint16_t v[2][kKeys * kVStride];   // [buf][key][dim] bf16: 2 x 20 KiB
+  float rowf[4][32];                 // per-wave row factors
 };
 constexpr size_t kPrefillLds = sizeof(PrefillLds);
 static_assert(sizeof(PrefillLds) >= 4 * 32 * kDim * 2, "epilogue staging fits");
@@ -105,11 +109,12 @@ __device__ __forceinline__ void load_k(const PrefillArgs& a, const int32_t* tabl
   }
 }
 
-// V tile t -> registers: 4 consecutive keys of one 8-dim chunk per thread.
+// V tile t -> registers: chunk tid & 15 of keys 4 (tid >> 4) .. +3, so that
+// 16 lanes read one key's whole 256-byte row.
 __device__ __forceinline__ void load_v(const PrefillArgs& a, const int32_t* table, int g, int ctx,
                                        int t, int tid, uint4 (&vr)[4]) {
   const TileGeom tg = tile_geom(a, table, g, ctx, t);
-  const int kq = tid & 15, ch = tid >> 4;
+  const int ch = tid & 15, kq = tid >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     vr[i] = buf_load16(tg.rv, uint32_t((tg.r0 + 4 * kq + i) * kChunks + ch) * 16u, 0u);
@@ -121,28 +126,12 @@ __device__ __forceinline__ void store_k(uint4* kbuf, int tid, const uint4 (&kx)[
   for (int j = 0; j < 4; ++j) kdst[256 * j] = kx[j];
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : (i == 1 ? u.y : (i == 2 ? u.z : u.w));
-}
-
-// V transposed to [dim][key]: each thread writes its 4 keys of each of its 8
-// dims as one 8-byte store.  Within 16 keys the order is the one the PV
-// operand reads (0-3, 8-11, 4-7, 12-15), so a lane's 8 keys of one k-step are
-// one 16-byte read.
-__device__ __forceinline__ void store_v(uint16_t* vtbuf, int tid, const uint4 (&vr)[4]) {
-  const int kq = tid & 15, ch = tid >> 4;
-  const int q = kq & 3;
-  const int pos = 16 * (kq >> 2) + 4 * (((q & 1) << 1) | (q >> 1));
-  uint2* base = reinterpret_cast<uint2*>(vtbuf + 8 * ch * kVtStride + pos);
+// V rows into LDS as they are ([key][dim], rows of kVStride): one 16-byte
+// store per chunk.
+__device__ __forceinline__ void store_v(uint16_t* vbuf, int tid, const uint4 (&vr)[4]) {
+  const int ch = tid & 15, kq = tid >> 4;
 #pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) {  // dims 2*e2, 2*e2+1 of the chunk
-    const uint32_t a0 = word_of(vr[0], e2), a1 = word_of(vr[1], e2);
-    const uint32_t a2 = word_of(vr[2], e2), a3 = word_of(vr[3], e2);
-    base[(2 * e2) * (kVtStride / 4)] =
-        make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-    base[(2 * e2 + 1) * (kVtStride / 4)] =
-        make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-  }
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(vbuf + (4 * kq + i) * kVStride + 8 * ch) = vr[i];
 }
 
 // Geometry of query block jrev (counted from the end) of sequence b, shared
@@ -296,6 +285,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int jl = lane & 15, dg = (lane >> 4) & 1;  // lane in its 16-lane group; dims 16 dg ..
 
   const BlockGeom<G> bg(a, b, jrev);
   if (jrev >= bg.nqb) return;
@@ -457,14 +447,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       pop[ks] = as_bf16x8(pb);
     }
 
-    // O += P V; lane reads dims 32n + col, keys 16ks + 4*half + {0..3, 8..11}
-    const uint16_t* vsrc = sm.vt[t & 1] + col * kVtStride + 8 * half;
+    // O += P V.  The B operand of lane (dim 32 n + col, half) is V of keys
+    // 16 ks + 4 half + {0..3} and 16 ks + 8 + 4 half + {0..3} (P's order),
+    // two transposing LDS reads: in each 16-lane group, lane j points at dims
+    // 4 (j & 3) .. +3 of key j >> 2 and receives its own dim of all 4 keys.
+    const uint16_t* vsrc = sm.v[t & 1] + (4 * half + (jl >> 2)) * kVStride + 16 * dg + 4 * (jl & 3);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int off = 32 * n * kVtStride + 16 * ks;  // bf16, compile-time
-        const bf16x8_t vop = as_bf16x8(*reinterpret_cast<const uint4*>(vsrc + off));
+        const int off0 = 16 * ks * kVStride + 32 * n;  // bf16, compile-time
+        const int off1 = off0 + 8 * kVStride;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off1));
+        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, both);
         o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], vop, o[n], 0, 0, 0);
       }
     }
@@ -474,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // Buffer t&1 last held tile t-2, which every wave finished computing
     // before the previous barrier.
     store_k(sm.k[t & 1], tid, kx);
-    store_v(sm.vt[t & 1], tid, vr);
+    store_v(sm.v[t & 1], tid, vr);
     if (t + 1 < t_end) {
       load_k(a, table, g, ctx, t + 1, tid, kx);
       load_v(a, table, g, ctx, t + 1, tid, vr);
