@@ -26,6 +26,9 @@
 //                 (ds_read_b64_tr_b16: in each 16-lane group, lane j points
 //                 at 4 dims of key j / 4 and receives dim j % 4 of the
 //                 group's 4 keys, so the group holds 16 dims x 4 keys).
+// Query blocks of at most 16 rows (a sequence with q_len x G <= 16) take a
+// separate path, described at prefill_short below.
+//
 // Online softmax in the log2 domain (scale*log2 e folded into one FMA) with a
 // lazy rescale: the reference max only moves when a row's max grows by more
 // than 2^8, so O is rescaled rarely.  Tiles entirely above a wave's diagonal
@@ -255,6 +258,251 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   }
 }
 
+
+// ---- short query blocks ----------------------------------------------------
+// A sequence whose rows all fit 16 (q_len x G <= 16: decode rows and a few
+// drafted tokens in a chunked-prefill batch) would leave most of a 128-row
+// workgroup idle and stream its context one tile per workgroup round trip.
+// Such a block takes its 16 rows (row v = token v / G, head v % G) as one
+// 16-row block of v_mfma_f32_16x16x32_bf16 in every wave, and each wave
+// streams a quarter of the part's key tiles on its own: K straight from
+// memory into A operands (chunk 4 ks + j of token 16 ms + l % 16), V into
+// the wave's own LDS rows and back through transposing reads in P's key
+// order, the next tile's loads in flight while one is computed.  The four
+// partial states (m, l, O) are then merged through LDS.  Such a block reads
+// each tile once (its rows share one kv head), so its loads take the
+// non-temporal policy, like the decode's.  Measured (one box, interleaved):
+// chunked prefill mixed with 64 decode rows 273.3 -> 260.2 us, 64 x 4
+// tokens 131.2 -> 115.9 us, 64 x 6 tokens 134.7 -> 122.0 us; the same path
+// with the default policy gained 1 % or nothing (the rows were waiting on
+// memory, not on the workgroup's bytes in flight).
+constexpr int kShortRows = 16;
+constexpr int kSVStride = 144;  // bf16 per V row in a wave's LDS (128 dims + pad, 288 B)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+static_assert(4 * kKeys * kSVStride * 2 + 4 * 16 * 4 <= sizeof(PrefillLds), "short-path LDS fits");
+static_assert(4 * (kShortRows * kDim + 2 * kShortRows) * 4 <= sizeof(PrefillLds), "short-path merge fits");
+
+// A 16-byte load with the non-temporal cache policy (NT bit of the buffer
+// builtins' cache-policy operand): the lines are not kept for reuse.
+__device__ __forceinline__ uint4 ld16nt(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float xor16_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned a = r[0], b = r[1];
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+template <int G>
+__device__ void prefill_short(const PrefillArgs& a, const BlockGeom<G>& bg, int b, int g, int part, int nsplit,
+                              int t_begin, int t_end, unsigned char* lds_raw) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int q0 = bg.q0, qlen = bg.qlen, ctx = bg.ctx, shift = bg.shift;
+  const int32_t* table = a.block_table + int64_t(b) * a.mbps;
+  uint16_t* vbuf = reinterpret_cast<uint16_t*>(lds_raw) + w * (kKeys * kSVStride);
+  float* rowf = reinterpret_cast<float*>(lds_raw + 4 * kKeys * kSVStride * 2) + 16 * w;
+  const float c = fabsf(a.scale_log2);
+
+  // this lane's score row (column of S^T): v = col
+  const int tv = col / G, hv = col % G;
+  const bool real = tv < qlen;
+  const int lim = real ? min(shift + tv, ctx - 1) : -1;  // last visible key
+
+  uint4 qop[4];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        a.q + (int64_t(q0) + (real ? tv : 0)) * (int64_t(a.hq) * kDim) + int64_t(g * G + hv) * kDim);
+    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = real ? src[4 * ks + grp] : zero4();
+      u.x ^= flip;
+      u.y ^= flip;
+      u.z ^= flip;
+      u.w ^= flip;
+      qop[ks] = u;
+    }
+  }
+
+  const int n = t_end - t_begin;
+  const int w0 = t_begin + n * w / 4, w1 = t_begin + n * (w + 1) / 4;
+
+  uint4 kr[16], vr[16];
+  int valid = 0;
+  auto issue = [&](int t) {
+    const TileGeom tg = tile_geom(a, table, g, ctx, t);
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      const int key = 16 * ms + col;
+      const uint32_t off = key < tg.valid ? uint32_t(tg.r0 + key) * 16u + uint32_t(grp) * 4096u : kOutOfRange;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kr[4 * ms + ks] = ld16nt(tg.rk, off + uint32_t(ks) * 16384u);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      vr[i] = ld16nt(tg.rv, uint32_t((tg.r0 + 4 * i + grp) * kChunks + col) * 16u);
+    return tg.valid;
+  };
+  if (w0 < w1) valid = issue(w0);
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[nb][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  for (int t = w0; t < w1; ++t) {
+    const int key0 = t * kKeys;
+    f32x4_t s[4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[ms][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+        s[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[4 * ms + ks]), as_bf16x8(qop[ks]), s[ms], 0, 0, 0);
+    // this tile's V into the wave's LDS rows, then the next tile's loads
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(vbuf + (4 * i + grp) * kSVStride + 8 * col) = vr[i];
+    __builtin_amdgcn_wave_barrier();
+    const int cur_valid = valid;
+    if (t + 1 < w1) valid = issue(t + 1);
+
+    // mask keys past the row's last visible key and past the context
+    if (key0 + kKeys - 1 > lim || cur_valid < kKeys) {
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = 16 * ms + 4 * grp + r;
+          s[ms][r] = (key0 + kk <= lim && kk < cur_valid) ? s[ms][r] : -INFINITY;
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[ms][r]);
+    mt = xor32_max(xor16_max(mt)) * c;
+    const float mnew = fmaxf(m, mt);
+    const bool need = mnew > m + kLazyRescale;
+    if (__ballot(need) != 0) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
+      if (need) {
+        l *= alpha;
+        m = mnew;
+      }
+      if (grp == 0) rowf[col] = alpha;
+      __builtin_amdgcn_wave_barrier();
+      const float4 al = *reinterpret_cast<const float4*>(&rowf[4 * grp]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        o[nb][0] *= al.x;
+        o[nb][1] *= al.y;
+        o[nb][2] *= al.z;
+        o[nb][3] *= al.w;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    const float mref = m == -INFINITY ? 0.f : m;
+    bf16x8_t pop[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float pf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks][e], c, -mref));
+        pf[4 + e] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks + 1][e], c, -mref));
+      }
+      const uint4 pb = pack8(pf);
+      l = dot2_bf16(pb.x, kBf16OnePair, l);
+      l = dot2_bf16(pb.y, kBf16OnePair, l);
+      l = dot2_bf16(pb.z, kBf16OnePair, l);
+      l = dot2_bf16(pb.w, kBf16OnePair, l);
+      pop[ks] = as_bf16x8(pb);
+    }
+    // O += P V: lane (dim 16 nb + col, group grp) gathers keys 32 ks + 16 r +
+    // 4 grp + {0..3} with transposing reads (lane col points at dims 4 (col &
+    // 3) .. +3 of key 32 ks + 16 r + 4 grp + col / 4)
+    const uint16_t* vsrc = vbuf + (4 * grp + (col >> 2)) * kSVStride + 4 * (col & 3);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int off0 = 32 * ks * kSVStride + 16 * nb;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0 + 16 * kSVStride));
+        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[ks], __builtin_bit_cast(bf16x8_t, both), o[nb], 0, 0,
+                                                        0);
+      }
+    __builtin_amdgcn_wave_barrier();
+  }
+  const float ltot = xor32_sum(xor16_sum(l));
+
+  // ---- merge of the four waves' states through LDS ----
+  __syncthreads();  // every wave is done with its V rows
+  float* st = reinterpret_cast<float*>(lds_raw);
+  constexpr int kSt = kShortRows * kDim + 2 * kShortRows;  // floats per wave: O, m, l
+  {
+    float* my = st + w * kSt;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) my[(4 * grp + r) * kDim + 16 * nb + col] = o[nb][r];
+    if (grp == 0) {
+      my[kShortRows * kDim + col] = m;
+      my[kShortRows * kDim + kShortRows + col] = ltot;
+    }
+  }
+  __syncthreads();
+  const int row = tid >> 4, d0 = 8 * (tid & 15);  // 16 rows x 16 groups of 8 dims
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) M = fmaxf(M, st[k * kSt + kShortRows * kDim + row]);
+  const float ref = M == -INFINITY ? 0.f : M;
+  float L = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float f = __builtin_amdgcn_exp2f(st[k * kSt + kShortRows * kDim + row] - ref);
+    L = fmaf(st[k * kSt + kShortRows * kDim + kShortRows + row], f, L);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(st[k * kSt + row * kDim + d0 + e], f, acc[e]);
+  }
+  const int rt = row / G, rh = row % G;
+  if (rt >= qlen) return;
+  const int64_t orow = (int64_t(q0) + rt) * a.hq + g * G + rh;  // output / record row
+  if (nsplit > 1) {
+    const int64_t rr = int64_t(part) * a.total_q * a.hq + orow;
+    if ((tid & 15) == 0) *reinterpret_cast<float2*>(a.rec_ml + rr * 2) = make_float2(M, L);
+    float4* ro = reinterpret_cast<float4*>(a.rec_o + rr * kDim + d0);
+    ro[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    ro[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    return;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint4 val;
+  val.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  val.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  val.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  val.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(a.out + orow * kDim + d0) = val;
+}
+
 template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int QB = kRowsPerWG / G;  // positions per workgroup
@@ -316,6 +564,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   if (part >= nsplit) return;
   const int t_begin = int(int64_t(ntiles) * part / nsplit);
   const int t_end = int(int64_t(ntiles) * (part + 1) / nsplit);
+  if (qlen * G <= kShortRows) {
+    prefill_short<G>(a, bg, b, g, part, nsplit, t_begin, t_end, lds_raw);
+    return;
+  }
 
   // Q^T operand: dims 16*ks + 8*half .. +7 of the lane's row, 8 k-steps.
   // With a negative scale the sign goes into q (exact in bf16), so scores are

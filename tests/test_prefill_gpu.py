@@ -203,6 +203,18 @@ def test_prefill_negative_scale():
                        scale=-0.09))
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (4, 1)])
+def test_prefill_short_blocks_at_the_boundary(hq, hkv):
+    """Sequences whose rows (q_len x q heads per kv head) number 15, 16 and
+    17 -- the last two on either side of the 16-row path for short blocks --
+    and a single row, over contexts shorter than a tile, a few tiles and
+    long enough for the context split; a negative scale on the way."""
+    g = hq // hkv
+    ql = [max(1, 15 // g), max(1, 16 // g), 16 // g + 1, 1, 16 // g, 1]
+    ctx = [ql[0] + 30, ql[1] + 700, ql[2] + 3000, 1, ql[4] + 20000, 9000]
+    check(wl.make_case(f"short_{hq}_{hkv}", "prefill", 48 + hq, ctx, hq, hkv, q_lens=ql, scale=-0.08))
+
+
 def test_prefill_empty_sequences():
     case = wl.make_case("empty", "prefill", 43, [0, 7, 0, 129], 16, 8)
     check(case)
