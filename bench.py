@@ -1098,7 +1098,7 @@ def main(argv=None):
         print("[bench] extra prefill_8x2048", file=sys.stderr, flush=True)
         extra["prefill_8x2048"] = prefill_report(max(30, args.steps // 5), 3)
         for name in ("chunked_prefill_mixed", "multi_query_decode", "spec_verify_decode",
-                     "long_prefix_chunk"):
+                     "long_prefix_chunk", "long_chunk_with_decode"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(30, args.steps // 5), 3)
         print("[bench] extra chunked_prefill_mixed split by kernel", file=sys.stderr, flush=True)

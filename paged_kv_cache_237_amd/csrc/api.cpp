@@ -162,14 +162,19 @@ size_t decode_ws_bytes(int32_t batch, int32_t num_kv_heads, int group, int64_t w
 // batch * max_seqlen_q) the grid's blocks differ in length in ways only the
 // device sees (a chunked-prefill batch mixes one-token decode rows with long
 // chunks), and grid order can dispatch a long block after a round of short
-// ones.  A small kernel then sorts the items longest-first into the
-// workspace (plan_bytes) and the attention kernel takes them in that order.
-// Launches whose contexts fit 4 blocks (16 tiles per query block at most)
-// are left in grid order: no block is long enough to end the launch late.
+// ones, or a block far longer than the rest can end the launch alone.  A
+// small kernel then plans the launch on the device (prefill.hip): it cuts
+// blocks longer than the launch's share of tiles per slot into parts and
+// sorts the items longest-first into the workspace (plan_bytes); the
+// attention kernel takes them in that order and the last part of a cut
+// block to finish merges it.  Launches whose contexts fit 4 blocks (16 tiles per query block at
+// most) are left in grid order: no block is long enough to end the launch
+// late.
 struct PrefillSplit {
   int split_tiles, max_splits, nqb_max;
   size_t ml_bytes, o_bytes, plan_bytes;
   bool plan;
+  int64_t cands, plan_items;  // plan: query-block candidates, grid items
 };
 
 constexpr int64_t kPrefillSlots = 2 * 256;
@@ -219,12 +224,30 @@ PrefillSplit prefill_split(int32_t batch, int64_t total_q_rows, int32_t max_seql
     if (best > 0.7 * one) want = 1;
   }
   ps.max_splits = int(std::min<int64_t>(want, cap));
-  // items of the plan (and workgroups of its 1-D grid, at most 2^24 of 256
-  // threads)
-  const int64_t items = int64_t(batch) * ps.max_splits * ps.nqb_max;
+  // A plan (ragged query lengths, contexts beyond 4 blocks) decides the
+  // split on the device instead: parts of at least kPrefillSplitTiles tiles,
+  // at most kPrefillMaxSplits per block, records in 2 * slots slots of
+  // kPrefillRows rows per kv head (enough for any cut the plan makes).  Its
+  // grid holds every (query block) candidate plus the extra parts (fewer
+  // than 2 * slots / num_kv_heads), at most 2^24 workgroups of 256 threads.
+  ps.cands = int64_t(batch) * ps.nqb_max;
+  ps.plan_items = ps.cands + (2 * pa::kPlanShareDiv * slots + num_kv_heads - 1) / num_kv_heads;
   ps.plan = total_q_rows < int64_t(batch) * max_seqlen_q && max_blocks_per_seq > 4 &&
-            items * num_kv_heads < (int64_t(1) << 24);
-  ps.plan_bytes = ps.plan ? (size_t(pa::kPlanHeader + items) * sizeof(int32_t) + 255) & ~size_t(255) : 0;
+            ps.plan_items * num_kv_heads < (int64_t(1) << 24);
+  if (ps.plan) {
+    static_assert(kPrefillMaxSplits <= 16, "a plan item keeps its part in 4 bits");
+    ps.split_tiles = kPrefillSplitTiles;
+    ps.max_splits = kPrefillMaxSplits;
+    ps.plan_bytes =
+        (size_t(pa::kPlanHeader + ps.plan_items + ps.cands + 2 * pa::kPlanShareDiv * slots) * sizeof(int32_t) +
+         255) & ~size_t(255);
+    // (slot * Hkv + g) < 2 * kPlanShareDiv * slots
+    const size_t rows = size_t(2 * pa::kPlanShareDiv * slots) * pa::kPrefillRows;
+    ps.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+    ps.o_bytes = (rows * size_t(pa::kDim) * sizeof(float) + 255) & ~size_t(255);
+    return ps;
+  }
+  ps.plan_bytes = 0;
   if (ps.max_splits == 1) {
     ps.ml_bytes = ps.o_bytes = 0;
     return ps;
@@ -729,6 +752,10 @@ int pa_prefill(void* out, const void* q, const int32_t* cu_seqlens_q,
     a.rec_ml = ps.ml_bytes > 0 ? reinterpret_cast<float*>(wsb) : nullptr;
     a.rec_o = ps.o_bytes > 0 ? reinterpret_cast<float*>(wsb + ps.ml_bytes) : nullptr;
     a.plan = ps.plan ? reinterpret_cast<int32_t*>(wsb + ps.ml_bytes + ps.o_bytes) : nullptr;
+    a.plan_rec = ps.plan ? a.plan + pa::kPlanHeader + ps.plan_items : nullptr;
+    a.plan_cnt = ps.plan ? a.plan_rec + ps.cands : nullptr;
+    a.plan_items = int(ps.plan_items);
+    a.slots = int(kPrefillSlots);
     if (debug_checks_on()) {
       pa::SeqCheckArgs c{};
       c.ctx_lens = context_lens;

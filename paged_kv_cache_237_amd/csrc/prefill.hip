@@ -143,7 +143,8 @@ template <int G>
 struct BlockGeom {
   int q0, qlen, ctx, nqb, p0, shift, ntiles, nsplit;
 
-  __device__ __forceinline__ BlockGeom(const PrefillArgs& a, int b, int jrev) {
+  // split_tiles: the launch's part length (the host's, or the plan's)
+  __device__ __forceinline__ BlockGeom(const PrefillArgs& a, int b, int jrev, int split_tiles) {
     constexpr int QB = kRowsPerWG / G;
     q0 = a.cu_q[b];
     qlen = max(0, a.cu_q[b + 1] - q0);
@@ -156,14 +157,60 @@ struct BlockGeom {
     const int kend = min(shift + last_row + 1, ctx);
     ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
     // records exist only when they are sized for every row
-    nsplit = min(max((ntiles + a.split_tiles - 1) / a.split_tiles, 1), a.max_splits);
-    if (nsplit > 1 && int64_t(a.cu_q[a.batch]) > a.total_q) nsplit = 1;
+    nsplit = ntiles > split_tiles ? min((ntiles - 1) / split_tiles + 1, a.max_splits) : 1;
+    if (nsplit > 1 && a.plan == nullptr && int64_t(a.cu_q[a.batch]) > a.total_q) nsplit = 1;
   }
 };
 
+template <int G>
+__device__ __forceinline__ int nqb_max_of(const PrefillArgs& a) {
+  constexpr int QB = kRowsPerWG / G;
+  return (a.max_q + QB - 1) / QB;
+}
+
+// The launch's part length: the host's, or the one the plan chose on the
+// device (wave-uniform).
+__device__ __forceinline__ int split_tiles_of(const PrefillArgs& a) {
+  return a.plan != nullptr ? __builtin_amdgcn_readfirstlane(a.plan[1]) : a.split_tiles;
+}
+
+// Record rows of query block (b, jrev) at kv head g, part `part`: in grid
+// order, by query row and head, sized for max_splits parts of every row;
+// with a plan, in the record slots the plan gave the block (plan_rec),
+// kRowsPerWG rows per (slot, kv head).  rec_base is the wave-uniform row of
+// the block's row 0 and rec_off the offset of its row R (head R / QB,
+// position R % QB) from it, so that the records' buffer descriptors stay in
+// scalar registers and the rows go into the per-lane offset.
+template <int G>
+__device__ __forceinline__ int64_t rec_base(const PrefillArgs& a, int b, int jrev, int g, int part, int q0,
+                                            int p0) {
+  if (a.plan != nullptr) {
+    const int slot = a.plan_rec[b * nqb_max_of<G>(a) + jrev] + part;
+    return (int64_t(slot) * a.hkv + g) * kRowsPerWG;
+  }
+  return (int64_t(part) * a.total_q + q0 + p0) * a.hq + g * G;
+}
+template <int G>
+__device__ __forceinline__ int rec_off(const PrefillArgs& a, int R) {
+  constexpr int QB = kRowsPerWG / G;
+  return a.plan != nullptr ? R : (R % QB) * a.hq + R / QB;
+}
+
+// Records are written with the SC1 cache-policy bit (agent-coherent: not
+// kept dirty in an XCD's private L2) and, where the last part of a block to
+// finish merges them, read with it too.
+constexpr int kCpolAgent = 16;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor of the records from p on (rows reached through the
+// per-lane offset, a few MiB at most).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const float* p) {
+  return make_rsrc(p, 0x7FFFFFF0u);
+}
+
 // One part of a split query block: its rows' (m, l, O) to the records.
 template <int G>
-__device__ void write_part(const PrefillArgs& a, int g, int part, int q0, int qlen, int p0,
+__device__ void write_part(const PrefillArgs& a, int b, int jrev, int g, int part, int q0, int qlen, int p0,
                            const f32x16_t (&o)[4], float m, float ltot) {
   constexpr int QB = kRowsPerWG / G;
   const int tid = threadIdx.x;
@@ -171,15 +218,21 @@ __device__ void write_part(const PrefillArgs& a, int g, int part, int q0, int ql
   const int w = tid >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int64_t pbase = int64_t(part) * a.total_q * a.hq;  // first record row of this part
-  auto rec_row = [&](int R) -> int64_t {
-    return pbase + (int64_t(q0) + p0 + R % QB) * a.hq + g * G + R / QB;
-  };
+  const int64_t base = rec_base<G>(a, b, jrev, g, part, q0, p0);
+  const __amdgpu_buffer_rsrc_t rm = rec_rsrc(a.rec_ml + base * 2);
+  const __amdgpu_buffer_rsrc_t ro = rec_rsrc(a.rec_o + base * kDim);
+  const bool coherent = a.plan != nullptr;  // merged by the last part to finish
   // (m, l): lane (col, half 0) owns row w*32 + col
   {
     const int R = w * 32 + col;
-    if (half == 0 && p0 + R % QB < qlen)
-      *reinterpret_cast<float2*>(a.rec_ml + rec_row(R) * 2) = make_float2(m, ltot);
+    if (half == 0 && p0 + R % QB < qlen) {
+      const u32x2_t v = {__float_as_uint(m), __float_as_uint(ltot)};
+      const int off = rec_off<G>(a, R) * 8;
+      if (coherent)
+        __builtin_amdgcn_raw_buffer_store_b64(v, rm, off, 0, kCpolAgent);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(v, rm, off, 0, 0);
+    }
   }
   // O: register 4*qd + i of o[n] is row 8*qd + 4*half + i of the wave, dim 32*n + col
 #pragma unroll
@@ -188,76 +241,138 @@ __device__ void write_part(const PrefillArgs& a, int g, int part, int q0, int ql
     for (int i = 0; i < 4; ++i) {
       const int R = w * 32 + 8 * qd + 4 * half + i;
       if (p0 + R % QB < qlen) {
-        float* ro = a.rec_o + rec_row(R) * kDim + col;
+        const int off = rec_off<G>(a, R) * (kDim * 4) + 4 * col;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) ro[32 * n] = o[n][4 * qd + i];
+        for (int n = 0; n < 4; ++n) {
+          const unsigned v = __float_as_uint(o[n][4 * qd + i]);
+          if (coherent)
+            __builtin_amdgcn_raw_buffer_store_b32(v, ro, off + 128 * n, 0, kCpolAgent);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(v, ro, off + 128 * n, 0, 0);
+        }
       }
     }
 }
 
-// Merge of split query blocks: workgroup (b, g, z) takes rows 64*(z&1) ..
-// +63 of block z/2; thread (r8, d4) rows r8 + 8i (i < 8), dims 4*d4 .. +3.
-// All loads of one part for the thread's 8 rows are independent and issued
-// together; parts are folded in with an online rescale.
-template <int G>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+// Merge of 64 * H rows (from row 64 * r0) of split query block (b, jrev) at
+// kv head g: thread (r8, d4) rows r0 * 64 + r8 + 8i (i < 8 H), dims 4*d4 ..
+// +3.  The loads of one part for all the thread's rows are issued together,
+// and those of part s + 1 before part s is folded in (online rescale, in
+// part order).  Coherent: the records are read with SC1 loads (a merge by
+// the last part to finish, in the same kernel as the other parts).
+template <int G, int H, bool Coherent>
+__device__ void merge_rows(const PrefillArgs& a, const BlockGeom<G>& bg, int b, int jrev, int g, int r0) {
   constexpr int QB = kRowsPerWG / G;
-  const int b = blockIdx.x, g = blockIdx.y;
-  const int jrev = blockIdx.z >> 1, rhalf = blockIdx.z & 1;
-  const BlockGeom<G> bg(a, b, jrev);
-  if (jrev >= bg.nqb || bg.nsplit <= 1) return;
+  constexpr int NR = 8 * H;  // rows per thread
   const int r8 = threadIdx.x >> 5, d4 = threadIdx.x & 31;
-  const int64_t pstride = a.total_q * a.hq;
-  int64_t rr[8];
-  bool ok[8];
+  int Rs[NR];
+  bool ok[NR];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int R = 64 * rhalf + r8 + 8 * i;
-    ok[i] = bg.p0 + R % QB < bg.qlen;
-    rr[i] = (int64_t(bg.q0) + bg.p0 + R % QB) * a.hq + g * G + R / QB;
+  for (int i = 0; i < NR; ++i) {
+    Rs[i] = 64 * r0 + r8 + 8 * i;
+    ok[i] = bg.p0 + Rs[i] % QB < bg.qlen;
   }
-  float M[8], L[8], acc[8][4];
+  float M[NR], L[NR], acc[NR][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NR; ++i) {
     M[i] = -INFINITY;
     L[i] = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
   }
-  for (int s = 0; s < bg.nsplit; ++s) {
-    float2 ml[8];
-    float4 u[8];
+  struct Part {
+    u32x2_t ml[NR];
+    u32x4_t u[NR];
+  };
+  int offs[NR];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = s * pstride + (ok[i] ? rr[i] : 0);
-      ml[i] = *reinterpret_cast<const float2*>(a.rec_ml + r * 2);
-      u[i] = *reinterpret_cast<const float4*>(a.rec_o + r * kDim + 4 * d4);
+  for (int i = 0; i < NR; ++i) offs[i] = rec_off<G>(a, ok[i] ? Rs[i] : 0);
+  auto load = [&](int s, Part& p) {
+    const int64_t base = rec_base<G>(a, b, jrev, g, s, bg.q0, bg.p0);
+    const __amdgpu_buffer_rsrc_t rm = rec_rsrc(a.rec_ml + base * 2);
+    const __amdgpu_buffer_rsrc_t ro = rec_rsrc(a.rec_o + base * kDim);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      p.ml[i] = __builtin_amdgcn_raw_buffer_load_b64(rm, offs[i] * 8, 0, Coherent ? kCpolAgent : 0);
+      p.u[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, offs[i] * (kDim * 4) + 16 * d4, 0,
+                                                     Coherent ? kCpolAgent : 0);
     }
+  };
+  Part cur, nxt;
+  load(0, cur);
+  for (int s = 0; s < bg.nsplit; ++s) {
+    if (s + 1 < bg.nsplit) load(s + 1, nxt);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float mn = fmaxf(M[i], ml[i].x);
+    for (int i = 0; i < NR; ++i) {
+      const unsigned m0 = cur.ml[i].x, l0 = cur.ml[i].y;
+      const float pm = __uint_as_float(m0), pl = __uint_as_float(l0);
+      const float mn = fmaxf(M[i], pm);
       if (mn == -INFINITY) continue;  // no visible key in any part so far
       const float fo = __builtin_amdgcn_exp2f(M[i] - mn);  // 0 while M is -inf
-      const float fs = __builtin_amdgcn_exp2f(ml[i].x - mn);
-      L[i] = L[i] * fo + ml[i].y * fs;
-      acc[i][0] = acc[i][0] * fo + u[i].x * fs;
-      acc[i][1] = acc[i][1] * fo + u[i].y * fs;
-      acc[i][2] = acc[i][2] * fo + u[i].z * fs;
-      acc[i][3] = acc[i][3] * fo + u[i].w * fs;
+      const float fs = __builtin_amdgcn_exp2f(pm - mn);
+      const unsigned x = cur.u[i].x, y = cur.u[i].y, z = cur.u[i].z, w = cur.u[i].w;
+      L[i] = L[i] * fo + pl * fs;
+      acc[i][0] = acc[i][0] * fo + __uint_as_float(x) * fs;
+      acc[i][1] = acc[i][1] * fo + __uint_as_float(y) * fs;
+      acc[i][2] = acc[i][2] * fo + __uint_as_float(z) * fs;
+      acc[i][3] = acc[i][3] * fo + __uint_as_float(w) * fs;
       M[i] = mn;
     }
+    if (s + 1 < bg.nsplit) cur = nxt;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NR; ++i) {
     if (!ok[i]) continue;
+    const int R = Rs[i];
     const float inv = L[i] > 0.f ? 1.f / L[i] : 0.f;
     // record row (q row, head) = output row
-    uint2* dst = reinterpret_cast<uint2*>(a.out + rr[i] * kDim + 4 * d4);
+    const int64_t orow = (int64_t(bg.q0) + bg.p0 + R % QB) * a.hq + g * G + R / QB;
+    uint2* dst = reinterpret_cast<uint2*>(a.out + orow * kDim + 4 * d4);
     *dst = make_uint2(pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv),
                       pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv));
   }
 }
 
+// Merge kernel of a launch in grid order (the host's split): workgroup
+// (b, g, z) takes rows 64*(z&1) .. +63 of block z/2.  The kernel boundary
+// makes the records visible.
+template <int G>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int jrev = blockIdx.z >> 1, rhalf = blockIdx.z & 1;
+  const BlockGeom<G> bg(a, b, jrev, a.split_tiles);
+  if (jrev >= bg.nqb || bg.nsplit <= 1) return;
+  merge_rows<G, 1, false>(a, bg, b, jrev, g, rhalf);
+}
+
+// With a plan, the parts of a cut block merge without a second kernel: each
+// part, once its records are written, counts its arrival on the block's
+// counter (zeroed by the plan kernel), and the last to arrive merges.  Why
+// that part sees every record (the ordering the one-row decode relies on as
+// well): every wave waits until its SC1 record stores are complete (s_waitcnt
+// vmcnt(0)), the workgroup barrier follows, and only then is the arrival
+// issued, an atomic performed at the memory side; the part that merges has
+// seen every other arrival, hence every other part's completed stores, and
+// it reads the records with SC1 loads, which do not hit a line another XCD's
+// L2 may hold.
+template <int G>
+__device__ void arrive_and_merge(const PrefillArgs& a, const BlockGeom<G>& bg, int b, int jrev, int g) {
+  __shared__ int last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's record stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int slot = a.plan_rec[b * nqb_max_of<G>(a) + jrev];
+    const int prev = __hip_atomic_fetch_add(a.plan_cnt + slot * a.hkv + g, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == bg.nsplit - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  merge_rows<G, 1, true>(a, bg, b, jrev, g, 0);
+  merge_rows<G, 1, true>(a, bg, b, jrev, g, 1);
+}
 
 // ---- short query blocks ----------------------------------------------------
 // A sequence whose rows all fit 16 (q_len x G <= 16: decode rows and a few
@@ -484,16 +599,35 @@ __device__ void prefill_short(const PrefillArgs& a, const BlockGeom<G>& bg, int 
     for (int e = 0; e < 8; ++e) acc[e] = fmaf(st[k * kSt + row * kDim + d0 + e], f, acc[e]);
   }
   const int rt = row / G, rh = row % G;
-  if (rt >= qlen) return;
-  const int64_t orow = (int64_t(q0) + rt) * a.hq + g * G + rh;  // output / record row
   if (nsplit > 1) {
-    const int64_t rr = int64_t(part) * a.total_q * a.hq + orow;
-    if ((tid & 15) == 0) *reinterpret_cast<float2*>(a.rec_ml + rr * 2) = make_float2(M, L);
-    float4* ro = reinterpret_cast<float4*>(a.rec_o + rr * kDim + d0);
-    ro[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    ro[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (rt < qlen) {
+      // the block's row R = head * QB + position, as the merge takes it
+      const int64_t base = rec_base<G>(a, b, 0, g, part, q0, 0);
+      const int off = rec_off<G>(a, rh * (kRowsPerWG / G) + rt);
+      const __amdgpu_buffer_rsrc_t rm = rec_rsrc(a.rec_ml + base * 2);
+      const __amdgpu_buffer_rsrc_t ro = rec_rsrc(a.rec_o + base * kDim);
+      const int om = off * 8, oo = off * (kDim * 4) + 4 * d0;
+      const u32x2_t v = {__float_as_uint(M), __float_as_uint(L)};
+      const u32x4_t lo = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                          __float_as_uint(acc[3])};
+      const u32x4_t hi = {__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
+                          __float_as_uint(acc[7])};
+      if (a.plan != nullptr) {  // merged by the last part to finish
+        if ((tid & 15) == 0) __builtin_amdgcn_raw_buffer_store_b64(v, rm, om, 0, kCpolAgent);
+        __builtin_amdgcn_raw_buffer_store_b128(lo, ro, oo, 0, kCpolAgent);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, ro, oo + 16, 0, kCpolAgent);
+      } else {
+        if ((tid & 15) == 0) __builtin_amdgcn_raw_buffer_store_b64(v, rm, om, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(lo, ro, oo, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, ro, oo + 16, 0, 0);
+      }
+    }
+    // every thread reaches the arrival's barriers
+    if (a.plan != nullptr) arrive_and_merge<G>(a, bg, b, 0, g);
     return;
   }
+  if (rt >= qlen) return;
+  const int64_t orow = (int64_t(q0) + rt) * a.hq + g * G + rh;  // output row
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint4 val;
   val.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
@@ -516,12 +650,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int k = int(blockIdx.x) / a.hkv;
     g = int(blockIdx.x) - k * a.hkv;
     if (k >= a.plan[0]) return;
-    const int id = a.plan[kPlanHeader + k];
-    const int nx = a.batch * a.max_splits;
-    jrev = id / nx;
-    const int x = id - jrev * nx;
-    b = x / a.max_splits;
-    part = x - b * a.max_splits;
+    const int id = a.plan[kPlanHeader + k];  // (b * nqb_max + jrev) * 16 + part
+    const int c = id >> 4, nq = nqb_max_of<G>(a);
+    part = id & 15;
+    b = c / nq;
+    jrev = c - b * nq;
   } else {
     b = int(blockIdx.x) / a.max_splits;
     part = int(blockIdx.x) - b * a.max_splits;
@@ -535,7 +668,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int half = lane >> 5;
   const int jl = lane & 15, dg = (lane >> 4) & 1;  // lane in its 16-lane group; dims 16 dg ..
 
-  const BlockGeom<G> bg(a, b, jrev);
+  const BlockGeom<G> bg(a, b, jrev, split_tiles_of(a));
   if (jrev >= bg.nqb) return;
   const int q0 = bg.q0, qlen = bg.qlen, ctx = bg.ctx, p0 = bg.p0, shift = bg.shift;
   const int ntiles = bg.ntiles, nsplit = bg.nsplit;
@@ -739,7 +872,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   const float ltot = xor32_sum(l);
   if (nsplit > 1) {
-    write_part<G>(a, g, part, q0, qlen, p0, o, m, ltot);
+    write_part<G>(a, b, jrev, g, part, q0, qlen, p0, o, m, ltot);
+    if (a.plan != nullptr) arrive_and_merge<G>(a, bg, b, jrev, g);
     return;
   }
 
@@ -780,46 +914,92 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// Longest-first order of the workgroup items (sequence, part, query block)
-// of a launch whose blocks differ in length on the device (ragged query
-// lengths): the hardware dispatches workgroups in grid order as slots free
-// up, so a long block dispatched after the first round of short ones ends
-// the launch late.  One workgroup counts the items per length (tiles of
-// their part, lengths of kPlanBuckets - 1 tiles and more counted together),
-// turns the counts into offsets in order of decreasing length, and writes
-// every item at its offset; items of one length keep no particular order
-// (each writes its own rows, so the outputs do not depend on it).
+// Plan of a launch whose blocks differ in length on the device (ragged
+// query lengths), in one workgroup:
+// * the part length: the hardware dispatches workgroups in grid order as
+//   slots free up, and one block streaming far more tiles than the launch's
+//   share per slot ends the launch late.  With W the tiles of all query
+//   blocks and kv heads, a block of more than L = max(split_tiles, ceil(W /
+//   slots)) tiles is cut into ceil(tiles / L) parts (at most max_splits) of
+//   near-equal length, merged afterwards; each cut block gets consecutive
+//   record slots (plan_rec).
+//   Every cut block has more than L tiles, so the cut blocks number fewer
+//   than W / L <= slots / hkv and their parts fewer than 2 W / L <= 2 slots /
+//   hkv: the records the host sizes for 2 slots x kRowsPerWG rows suffice.
+//   The parts merge without a second kernel (arrive_and_merge); the plan
+//   zeroes their arrival counters (plan_cnt, one per first slot and kv head).
+// * the order: the items (query block, part) counted per length (tiles of
+//   the part; kPlanBuckets - 1 and more counted together), the counts turned
+//   into offsets in order of decreasing length, every item written at its
+//   offset; items of one length keep no particular order and record slots
+//   go to cut blocks in no particular order (each item writes its own rows
+//   or records, and the merge reads a block's parts in part order, so the
+//   outputs do not depend on either).
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 4096;
 
 template <int G>
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a) {
-  constexpr int QB = kRowsPerWG / G;
   __shared__ int cnt[kPlanBuckets];  // per key = kPlanBuckets - 1 - min(length, kPlanBuckets - 1)
   __shared__ int wsum[kPlanThreads / 64];
+  __shared__ long long wtiles[kPlanThreads / 64];
+  __shared__ int n_slots, n_cut, split_len;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   for (int i = tid; i < kPlanBuckets; i += kPlanThreads) cnt[i] = 0;
-  __syncthreads();
+  if (tid == 0) {
+    n_slots = 0;
+    n_cut = 0;
+  }
 
-  const int nqb_max = (a.max_q + QB - 1) / QB;
+  const int nqb_max = nqb_max_of<G>(a);
   const int64_t cands = int64_t(a.batch) * nqb_max;
-  const int nx = a.batch * a.max_splits;
-  // fn(item id, key) for every item of the launch
-  auto for_items = [&](auto&& fn) {
+
+  // W: tiles of every query block (one kv head)
+  long long mine = 0;
+  for (int64_t c = tid; c < cands; c += kPlanThreads) {
+    const int b = int(c / nqb_max);
+    const int jrev = int(c - int64_t(b) * nqb_max);
+    const BlockGeom<G> bg(a, b, jrev, INT32_MAX);
+    if (jrev < bg.nqb) mine += bg.ntiles;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mine += __shfl_xor(mine, d, 64);
+  if (lane == 0) wtiles[w] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    long long wt = 0;
+    for (int i = 0; i < kPlanThreads / 64; ++i) wt += wtiles[i];
+    const long long den = (long long)a.slots * kPlanShareDiv;
+    long long share = (wt * a.hkv + den - 1) / den;
+    share = share < a.split_tiles ? a.split_tiles : share;
+    split_len = int(share > INT32_MAX ? INT32_MAX : share);
+    a.plan[1] = split_len;
+  }
+  __syncthreads();
+  const int L = split_len;
+
+  // fn(item id, key) for every item of the launch; cut blocks get their
+  // record slots and merge-list places on the way (first pass only)
+  auto for_items = [&](bool first, auto&& fn) {
     for (int64_t c = tid; c < cands; c += kPlanThreads) {
       const int b = int(c / nqb_max);
       const int jrev = int(c - int64_t(b) * nqb_max);
-      const BlockGeom<G> bg(a, b, jrev);
+      const BlockGeom<G> bg(a, b, jrev, L);
       if (jrev >= bg.nqb) continue;
-      for (int part = 0; part < bg.nsplit; ++part) {
-        const int len = int(int64_t(bg.ntiles) * (part + 1) / bg.nsplit) -
-                        int(int64_t(bg.ntiles) * part / bg.nsplit);
-        fn(jrev * nx + b * a.max_splits + part, kPlanBuckets - 1 - min(len, kPlanBuckets - 1));
+      if (first && bg.nsplit > 1) {
+        const int slot = atomicAdd(&n_slots, bg.nsplit);
+        a.plan_rec[c] = slot;
+        atomicAdd(&n_cut, 1);
+        for (int g = 0; g < a.hkv; ++g) a.plan_cnt[slot * a.hkv + g] = 0;  // arrival counters
       }
+      // the parts of a cut block go by the whole block's length, so that
+      // they start in the first round rather than after every longer item
+      for (int part = 0; part < bg.nsplit; ++part)
+        fn(int(c) * 16 + part, kPlanBuckets - 1 - min(bg.ntiles, kPlanBuckets - 1));
     }
   };
-  for_items([&](int, int key) { atomicAdd(&cnt[key], 1); });
+  for_items(true, [&](int, int key) { atomicAdd(&cnt[key], 1); });
   __syncthreads();
 
   // exclusive scan of the counts in key order: thread t owns keys 4t .. 4t+3
@@ -850,11 +1030,14 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
     cnt[kPer * tid + i] = off;
     off += c4[i];
   }
-  if (tid == 0) a.plan[0] = total;
+  if (tid == 0) {
+    a.plan[0] = total;
+    a.plan[2] = n_cut;
+  }
   __syncthreads();
 
   int32_t* order = a.plan + kPlanHeader;
-  for_items([&](int id, int key) { order[atomicAdd(&cnt[key], 1)] = id; });
+  for_items(false, [&](int id, int key) { order[atomicAdd(&cnt[key], 1)] = id; });
 }
 
 template <int G>
@@ -868,15 +1051,16 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.max_q + QB - 1) / QB;
   if (a.plan != nullptr) {
     hipLaunchKernelGGL(prefill_plan_kernel<G>, dim3(1), dim3(kPlanThreads), 0, s, a);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // as many workgroups as the grid below holds; those past the count exit
-    const unsigned n = unsigned(a.batch) * unsigned(a.max_splits) * unsigned(nqb) * unsigned(a.hkv);
-    hipLaunchKernelGGL(prefill_kernel<G>, dim3(n), dim3(256), kPrefillLds, s, a);
-  } else {
-    const dim3 grid(unsigned(a.batch) * unsigned(a.max_splits), unsigned(a.hkv), unsigned(nqb));
-    hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), kPrefillLds, s, a);
+    // workgroups for every possible item (kv head fastest); those past the
+    // plan's count exit at once
+    hipLaunchKernelGGL(prefill_kernel<G>, dim3(unsigned(a.plan_items) * unsigned(a.hkv)), dim3(256),
+                       kPrefillLds, s, a);
+    return hipGetLastError();
   }
+  const dim3 grid(unsigned(a.batch) * unsigned(a.max_splits), unsigned(a.hkv), unsigned(nqb));
+  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(256), kPrefillLds, s, a);
   if (a.max_splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

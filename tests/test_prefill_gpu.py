@@ -136,6 +136,26 @@ def test_long_prefix_chunk():
     check(case, seqs_full=set(), heads_sampled=[0, 5, 15])
 
 
+def test_prefill_plan_cuts_a_long_block():
+    """A 512-token chunk over a 32,768-token prefix beside 63 one-token
+    decode rows: the plan cuts the chunk's query blocks into parts (records
+    in the plan's slots), the last part of each to finish merges it; the
+    decode rows take the 16-row path."""
+    case = wl.long_chunk_with_decode()
+    check(case, seqs_full=set(range(1, case.batch)), heads_sampled=[0, 9, 15])
+
+
+def test_prefill_plan_cuts_two_long_blocks_among_chunks():
+    """Two 512-token chunks over 16K- and 12K-token prefixes among thirty
+    256-token chunks over U{1024..4096}-token prefixes: only the long chunks'
+    blocks exceed the launch's share of tiles per slot and are cut."""
+    rng = np.random.default_rng(34)
+    ctx = np.concatenate([[16384 + 512, 12288 + 512], rng.integers(1024, 4096, size=30, endpoint=True) + 256])
+    ql = np.concatenate([[512, 512], np.full(30, 256)])
+    case = wl.make_case("plan_two_long", "prefill", 34, ctx, 16, 8, q_lens=ql, rng=rng)
+    check(case, seqs_full=set(range(2, 32, 5)), heads_sampled=[0, 7, 15])
+
+
 def test_prefill_split_repeat_is_bit_identical():
     """Two calls on one workspace give the same bits: the merge order is
     fixed and nothing depends on what the workspace held before."""

@@ -364,6 +364,18 @@ def long_prefix_chunk() -> PagedCase:
     return make_case("long_prefix_chunk", "prefill", 8, [65536 + 512], 16, 8, q_lens=[512])
 
 
+def long_chunk_with_decode() -> PagedCase:
+    """Chunked prefill beside a decode batch when one prompt is far longer
+    than the rest: a 512-token chunk on top of a 32,768-token cached prefix
+    and 63 sequences decoding one token over U{512..4096} cached tokens;
+    16 q / 8 kv heads.  The chunk comes first in the batch."""
+    rng = np.random.default_rng(33)
+    dctx = rng.integers(512, 4096, size=63, endpoint=True)
+    ctx = np.concatenate([[32768 + 512], dctx])
+    ql = np.concatenate([[512], np.ones(63, dtype=np.int64)])
+    return make_case("long_chunk_with_decode", "prefill", 33, ctx, 16, 8, q_lens=ql, rng=rng)
+
+
 CONFIGS = {
     "tiny_decode": tiny_decode,
     "qwen3_0.6b_decode": qwen3_0_6b_decode,
@@ -374,6 +386,7 @@ CONFIGS = {
     "multi_query_decode": multi_query_decode,
     "long_prefix_chunk": long_prefix_chunk,
     "spec_verify_decode": spec_verify_decode,
+    "long_chunk_with_decode": long_chunk_with_decode,
 }
 
 
