@@ -125,6 +125,21 @@ def test_decode_multi_long_contexts_cut_across_waves(hq):
     check(case, 6)
 
 
+@pytest.mark.parametrize("hq,ql", [(16, 2), (16, 6), (32, 6)])
+def test_decode_multi_block_permutation_gives_identical_bits(hq, ql):
+    """Same logical contents under another physical placement, on each of
+    the three decode-multi kernels (4, 12 and 24 rows per kv head): the
+    split plan depends only on the lengths, so the bits are identical."""
+    lens = [ql, 700, 3000, 257, 9000]
+    c1 = wl.make_case(f"perm_m{hq}_{ql}", "prefill", 91, lens, hq, 8, q_lens=[ql] * 5, num_blocks=60)
+    c2 = wl.make_case(f"perm_m{hq}_{ql}", "prefill", 91, lens, hq, 8, q_lens=[ql] * 5, num_blocks=60,
+                      rng=np.random.default_rng(997))
+    assert not np.array_equal(c1.block_table, c2.block_table)
+    o1 = run_multi(place(c1), ql)
+    o2 = run_multi(place(c2), ql)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_decode_multi_negative_scale():
     """A negative logit scale (allowed: finite) on the three decode-multi
     kernels (4, 12 and 24 rows per kv head)."""

@@ -156,6 +156,21 @@ def test_prefill_plan_cuts_two_long_blocks_among_chunks():
     check(case, seqs_full=set(range(2, 32, 5)), heads_sampled=[0, 7, 15])
 
 
+def test_prefill_block_permutation_gives_identical_bits():
+    """Same logical contents under another physical placement of the blocks:
+    a ragged batch with a long prefix (planned, cut and merged), a short
+    row and a plain prompt gives bit-identical outputs."""
+    lens, ql = [9000 + 300, 40, 700, 3000], [300, 1, 700, 6]
+    c1 = wl.make_case("perm_p", "prefill", 49, lens, 16, 8, q_lens=ql, num_blocks=60)
+    c2 = wl.make_case("perm_p", "prefill", 49, lens, 16, 8, q_lens=ql, num_blocks=60,
+                      rng=np.random.default_rng(998))
+    assert not np.array_equal(c1.block_table, c2.block_table)
+    o1 = run_prefill(place(c1))
+    o2 = run_prefill(place(c2))
+    assert not torch.isnan(o1).any()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_prefill_split_repeat_is_bit_identical():
     """Two calls on one workspace give the same bits: the merge order is
     fixed and nothing depends on what the workspace held before."""
