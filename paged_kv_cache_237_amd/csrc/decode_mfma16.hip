@@ -36,10 +36,14 @@
 //   O += P V   : per 32 keys, A = bf16(P) straight from the accumulators of
 //                 key blocks 2 ks and 2 ks + 1 (lane group j holds keys 4 j ..
 //                 4 j + 3 and 16 + 4 j .. 16 + 4 j + 3, taken as k = 8 j ..
-//                 8 j + 7); V is stored transposed in LDS with each 32 keys
-//                 in that order, so a lane's B operand (dim l % 16) is one
-//                 16-byte read.  The accumulator of dim block n holds dims
-//                 16 n + l % 16, rows 4 j .. 4 j + 3.
+//                 8 j + 7); V is kept in the wave's LDS as it arrives (one row
+//                 per token), and a lane's B operand (its dim l % 16 of those
+//                 8 keys) is two transposing reads (ds_read_b64_tr_b16), as in
+//                 the prefill.  Against a transposed V tile (permutes and
+//                 8-byte stores): 64 x 6 tokens 129.1 -> 127.5 us, long
+//                 contexts unchanged (one box, interleaved).  The
+//                 accumulator of dim block n holds dims 16 n + l % 16, rows
+//                 4 j .. 4 j + 3.
 #include <math.h>
 
 #include "decode_mfma_common.hpp"
@@ -48,13 +52,15 @@ namespace pa {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 constexpr int kM16Rows = 16;   // rows per segment: one 16-row MFMA block
 constexpr int kM16Waves = 4;   // waves per workgroup, one per SIMD
 static_assert(partial_floats(kM16Rows) == kM16Rows * (kDim + 2), "record layout");
 
-// One wave's LDS: the transposed V tile (also the output staging at the end
-// of a piece) and per-row factors exchanged between lanes.
+// One wave's LDS: the V tile (also the output staging at the end of a
+// piece) and per-row factors exchanged between lanes.
 struct M16Lds {
   uint16_t vt[kDim * kMfVtStride];
   float rowf[kM16Rows];
@@ -81,28 +87,18 @@ __device__ __forceinline__ void m16_issue_k(const MfTile& tl, uint4 (&kr)[16]) {
 }
 
 // The tile's V (loaded by mf_issue_v: vr[4 j + i] = chunk lane & 15 of token
-// 4 kq + i, kq = (lane >> 4) + 4 j) into LDS as [dim][key], each 32 keys in
-// the order of the P operand: position 8 a + e holds key 4 a + e (e < 4) or
-// 16 + 4 a + e - 4 (e >= 4).  One 8-byte store per dim and 4-key group.
+// 16 j + 4 (lane >> 4) + i) into LDS as it is: rows of kM16VStride bf16 per
+// token, one 16-byte store per chunk.
+constexpr int kM16VStride = 144;  // 128 dims + pad (288 B): the transposing reads hit no bank twice
+static_assert(kTile * kM16VStride <= kDim * kMfVtStride, "V rows fit the wave's LDS");
 __device__ __forceinline__ void m16_store_v(uint16_t* vt, const uint4 (&vr)[16]) {
   const int lane = lane_id();
   const int ch = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kq = (lane >> 4) + 4 * j;  // tokens 4 kq .. 4 kq + 3 of the tile
-    const int q = kq & 7;
-    const int pos = 32 * (kq >> 3) + 8 * (q & 3) + 4 * (q >> 2);
-    uint2* base = reinterpret_cast<uint2*>(vt + 8 * ch * kMfVtStride + pos);
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {  // dims 2 e2 and 2 e2 + 1 of the chunk
-      const uint32_t a0 = word_at(vr[4 * j + 0], e2), a1 = word_at(vr[4 * j + 1], e2);
-      const uint32_t a2 = word_at(vr[4 * j + 2], e2), a3 = word_at(vr[4 * j + 3], e2);
-      base[(2 * e2) * (kMfVtStride / 4)] =
-          make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-      base[(2 * e2 + 1) * (kMfVtStride / 4)] =
-          make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-    }
-  }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(vt + (16 * j + 4 * (lane >> 4) + i) * kM16VStride + 8 * ch) = vr[4 * j + i];
 }
 
 // Q^T of segment (b, g) as B operands: dims 32 ks + 8 j .. +7 of row l % 16;
@@ -193,7 +189,7 @@ __device__ void m16_merge(const DecodeArgs& a, int seg, int b, int g, int w0, in
 
 // Streams tiles [pos, end) of the flattened list (this wave's run): the K
 // and V of tile i + 1 are loaded into the registers tile i frees (K after
-// its scores, V after its transposed store), so one tile is in flight while
+// its scores, V after its store to LDS), so one tile is in flight while
 // one is computed -- also across segment boundaries (block-table entries are
 // looked up a tile ahead; the next segment's q is loaded when a piece ends).
 // Each piece (run ∩ segment) ends with either the bf16 output (whole
@@ -339,13 +335,21 @@ __device__ int m16_stream_run(const DecodeArgs& a, const TileScan& sc, int pos, 
     }
 
     // --- O += P V (dims 16 n + col, P's keys of k-step ks in LDS order)
-    const uint16_t* vsrc = L.vt + col * kMfVtStride + 8 * grp;
+    // lane (dim 16 n + col, group grp) gathers keys 32 ks + 16 r + 4 grp +
+    // {0..3} with transposing reads: lane col points at dims 4 (col & 3) ..
+    // +3 of key 32 ks + 16 r + 4 grp + col / 4 and receives its own dim
+    const uint16_t* vsrc = L.vt + (4 * grp + (col >> 2)) * kM16VStride + 4 * (col & 3);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const bf16x8_t vop = as_bf8(*reinterpret_cast<const uint4*>(vsrc + 16 * n * kMfVtStride + 32 * ks));
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[ks], vop, o[n], 0, 0, 0);
+        const int off0 = 32 * ks * kM16VStride + 16 * n;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0 + 16 * kM16VStride));
+        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[ks], __builtin_bit_cast(bf16x8_t, both), o[n], 0, 0, 0);
       }
     lds_order();
 
