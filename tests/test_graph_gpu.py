@@ -1,6 +1,7 @@
 """Steps captured in a HIP graph and replayed: the decode step (pa_store_kv
 then pa_decode), a prefill whose query blocks are split across workgroups
-(attention and merge kernels), and pa_decode_multi.  Every replay must give
+(attention and merge kernels), a planned prefill whose cut blocks merge in
+the attention kernel, and pa_decode_multi.  Every replay must give
 the same bits as the eager calls, also with other eager work and
 synchronisations between replays.  The library's kernels use no memset
 nodes; the decode workspace counters are reset by the kernel itself and the
@@ -91,6 +92,28 @@ def test_graph_prefill_with_split_blocks():
     ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len,
                                     case.num_q_heads, case.num_kv_heads, case.max_blocks_per_seq)
     assert ws is not None  # the launch splits its query blocks
+
+    def step():
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        pa.prefill(out, dev.q, dev.cu_q, dev.context_lens, case.max_q_len, dev.k_cache,
+                   dev.v_cache, dev.block_table, case.scale, ws)
+
+    replay_and_check(step, out, case.name)
+
+
+def test_graph_prefill_planned_and_cut():
+    """A ragged batch (a 512-token chunk over a 32K-token prefix beside 63
+    decode rows): the plan kernel, the attention kernel with cut blocks
+    merged by their last part, and the short-row path, captured and
+    replayed; every replay's plan re-zeroes the arrival counters."""
+    case = wl.long_chunk_with_decode()
+    print(f"[graph] {case.name}", flush=True)
+    dev = place(case)
+    out = torch.zeros((case.total_q_rows, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    ws = pa.alloc_prefill_workspace(case.batch, case.total_q_rows, case.max_q_len,
+                                    case.num_q_heads, case.num_kv_heads, case.max_blocks_per_seq)
+    assert ws is not None  # the launch is planned
 
     def step():
         pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
