@@ -992,6 +992,12 @@ DEFAULT_WORKLOAD = "long_context_decode"
 DECODE_WORKLOADS = ("long_context_decode", "qwen3_4b_decode", "qwen3_0.6b_decode")
 
 
+# workloads --extra-only can time alone: pa_prefill batches, pa_decode_multi
+# batches, the block copies / swaps
+EXTRA_ONLY = ("chunked_prefill_mixed", "multi_query_decode", "spec_verify_decode", "long_prefix_chunk",
+              "long_chunk_with_decode", "multi_query_decode_multi", "spec_verify_decode_multi", "blocks")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1004,6 +1010,9 @@ def main(argv=None):
                     help="skip the graph-replay timings of the step (the headline step is eager)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time store + prefill of the 8 x 2048 prompt batch (for profiling)")
+    ap.add_argument("--extra-only", choices=EXTRA_ONLY, default=None,
+                    help="only time this one extra workload (for a kernel trace of it alone): a "
+                         "pa_prefill batch, a pa_decode_multi batch (suffix _multi) or the block copies")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -1048,6 +1057,16 @@ def main(argv=None):
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_report(args.steps, args.warmup)}), flush=True)
         copy_probe(args.copy_probe_mib)
+        return 0
+    if args.extra_only:
+        name = args.extra_only
+        if name == "blocks":
+            res = blocks_report(args.steps, args.warmup)
+        elif name.endswith("_multi"):
+            res = decode_multi_report(name[:-len("_multi")], args.steps, args.warmup)
+        else:
+            res = varlen_report(name, args.steps, args.warmup)
+        print(json.dumps({name: res}), flush=True)
         return 0
 
     case = wl.CONFIGS[args.workload]()
