@@ -357,12 +357,21 @@ def varlen_report(name: str, steps: int, warmup: int) -> dict:
     kvb = int(c.context_lens.sum()) * c.num_kv_heads * c.head_dim * 2 * 2
     tf = fl / (pre * 1e-3) / 1e12
     gbs = kvb / (pre * 1e-3) / 1e9
+    fm, fh = tf / BF16_MFMA_PEAK_TFLOPS, gbs / HBM_PEAK_GBS
+    # the roofline object names the side the batch is closer to (a batch of
+    # short rows reads K/V; one of long chunks computes)
+    roof = ({"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
+             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fm, 4),
+             "algorithmic_flops_per_launch": fl} if fm >= fh else
+            {"bound": "hbm", "kernel": "prefill_kernel", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": round(fh, 4), "algorithmic_kv_bytes_per_launch": kvb})
+    roof["traffic"] = None
     return {"workload": c.name, "prefill_ms": round(pre, 4), **PREFILL_SPREAD.get(c.name, {}),
             "query_rows": c.total_q_rows,
             "sum_context_len": int(c.context_lens.sum()), "causal_gflop": round(fl / 1e9, 3),
-            "TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-            "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "store_ms": round(sto, 4)}
+            "TFLOPs": round(tf, 1), "frac_of_bf16_mfma_peak": round(fm, 4),
+            "kv_GBps": round(gbs, 1), "frac_of_hbm_peak": round(fh, 4),
+            "store_ms": round(sto, 4), "roofline": roof}
 
 
 def mixed_split_report(steps: int, warmup: int) -> dict:
