@@ -1004,7 +1004,8 @@ DECODE_WORKLOADS = ("long_context_decode", "qwen3_4b_decode", "qwen3_0.6b_decode
 # workloads --extra-only can time alone: pa_prefill batches, pa_decode_multi
 # batches, the block copies / swaps
 EXTRA_ONLY = ("chunked_prefill_mixed", "multi_query_decode", "spec_verify_decode", "long_prefix_chunk",
-              "long_chunk_with_decode", "multi_query_decode_multi", "spec_verify_decode_multi", "blocks")
+              "long_chunk_with_decode", "multi_query_decode_multi", "spec_verify_decode_multi",
+              "spec_verify_decode_g4_multi", "blocks")
 
 
 def main(argv=None):
@@ -1131,7 +1132,7 @@ def main(argv=None):
             extra[name] = varlen_report(name, max(30, args.steps // 5), 3)
         print("[bench] extra chunked_prefill_mixed split by kernel", file=sys.stderr, flush=True)
         extra["chunked_prefill_mixed_split"] = mixed_split_report(max(30, args.steps // 5), 3)
-        for name in ("multi_query_decode", "spec_verify_decode"):
+        for name in ("multi_query_decode", "spec_verify_decode", "spec_verify_decode_g4"):
             print(f"[bench] extra {name} (pa_decode_multi)", file=sys.stderr, flush=True)
             extra[f"{name}_multi"] = decode_multi_report(name, max(20, args.steps // 5), 3)
         print("[bench] extra block copy / swap", file=sys.stderr, flush=True)

@@ -32,8 +32,14 @@
 //                 domain with a lazy rescale (the reference max moves only
 //                 when a row max grows by more than 2^8).
 //   O += P V   : P rounded to bf16 straight from the S^T accumulator (A
-//                 operand); V goes through the wave's own LDS, transposed to
-//                 [dim][key] in the accumulator's key order (B operand).
+//                 operand: lane half h holds keys 16 ks + 4 h + {0..3, 8..11}
+//                 of k-step ks); V is kept in the wave's LDS as it arrives,
+//                 one row per token, and a lane's B operand (its dim of those
+//                 8 keys) is two transposing reads (ds_read_b64_tr_b16).
+//                 Against a V tile transposed to [dim][key] on its way into
+//                 LDS (permutes and 8-byte stores): 64 x 6 tokens with 32 q
+//                 heads 133.1 -> 131.1 us, 131072-token contexts unchanged
+//                 (one box, interleaved).
 // The row sums add the bf16 weights the MFMA consumes.  Memory traffic is
 // the K and V rows of each context read once; the matrix work of a tile is a
 // small part of the time its 32 KiB take to arrive, so, like the one-row
@@ -55,10 +61,12 @@ constexpr int kMfWaves = 4;       // waves per workgroup, one per SIMD
 constexpr int kMfDepth = 1;
 static_assert(partial_floats(kMfRows) == kMfRows * (kDim + 2), "record layout");
 
-// One wave's LDS: the transposed V tile (also the output staging at the end
-// of a piece) and per-row factors exchanged between lanes.
+constexpr int kMfVStride = 160;  // bf16 per V row in LDS (128 dims + pad: the transposing reads hit no bank twice)
+
+// One wave's LDS: the V tile, one row per token (also the output staging at
+// the end of a piece), and per-row factors exchanged between lanes.
 struct MfLds {
-  uint16_t vt[kDim * kMfVtStride];
+  uint16_t vt[kTile * kMfVStride];
   float rowf[kMfRows];
 };
 
@@ -72,30 +80,6 @@ __device__ __forceinline__ void mf_issue_k(const MfTile& tl, uint4 (&kr)[16]) {
     const uint32_t off = key < tl.valid ? uint32_t(tl.r0 + key) * 16u + uint32_t(half) * 4096u : kOutOfRange;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kr[8 * ms + ks] = buf_load16_stream(tl.rk, off + uint32_t(ks) * 8192u, 0u);
-  }
-}
-
-// The tile's V into LDS as [dim][key], each 16 keys in the order the P
-// operand holds them (0-3, 8-11, 4-7, 12-15): one 8-byte store per dim and
-// 4-key group.
-__device__ __forceinline__ void mf_store_v(uint16_t* vt, const uint4 (&vr)[16]) {
-  const int lane = lane_id();
-  const int ch = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kq = (lane >> 4) + 4 * j;
-    const int q = kq & 3;
-    const int pos = 16 * (kq >> 2) + 4 * (((q & 1) << 1) | (q >> 1));
-    uint2* base = reinterpret_cast<uint2*>(vt + 8 * ch * kMfVtStride + pos);
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {  // dims 2 e2 and 2 e2 + 1 of the chunk
-      const uint32_t a0 = word_at(vr[4 * j + 0], e2), a1 = word_at(vr[4 * j + 1], e2);
-      const uint32_t a2 = word_at(vr[4 * j + 2], e2), a3 = word_at(vr[4 * j + 3], e2);
-      base[(2 * e2) * (kMfVtStride / 4)] =
-          make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-      base[(2 * e2 + 1) * (kMfVtStride / 4)] =
-          make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-    }
   }
 }
 
@@ -282,7 +266,7 @@ __device__ int mf_stream_run(const DecodeArgs& a, const TileScan& sc, int pos, i
 
     // --- V of this tile into LDS, then V of tile i + kMfDepth into its registers
     lds_order();
-    mf_store_v(L.vt, vr);
+    mf_store_v_rows<kMfVStride>(L.vt, vr);
     mf_issue_v(t2, vr);
     lds_order();
 
@@ -344,12 +328,16 @@ __device__ int mf_stream_run(const DecodeArgs& a, const TileScan& sc, int pos, i
     }
 
     // --- O += P V (dims 32 n + col, keys 16 ks + 4 half + {0..3, 8..11})
-    const uint16_t* vsrc = L.vt + col * kMfVtStride + 8 * half;
+    // within each 16-lane group (its dims 32 n + 16 dg .. + 15), lane jl
+    // points at dims 4 (jl & 3) .. + 3 of key 16 ks + 4 half + jl / 4; the
+    // second read takes the keys 8 further
+    const int jl = col & 15, dg = col >> 4;
+    const uint16_t* vsrc = L.vt + (4 * half + (jl >> 2)) * kMfVStride + 16 * dg + 4 * (jl & 3);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const bf16x8_t vop = as_bf8(*reinterpret_cast<const uint4*>(vsrc + 32 * n * kMfVtStride + 16 * ks));
+        const bf16x8_t vop = tr_read_pair(vsrc + 16 * ks * kMfVStride + 32 * n, 8 * kMfVStride);
         o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], vop, o[n], 0, 0, 0);
       }
     lds_order();

@@ -52,17 +52,17 @@ namespace pa {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 constexpr int kM16Rows = 16;   // rows per segment: one 16-row MFMA block
 constexpr int kM16Waves = 4;   // waves per workgroup, one per SIMD
 static_assert(partial_floats(kM16Rows) == kM16Rows * (kDim + 2), "record layout");
 
-// One wave's LDS: the V tile (also the output staging at the end of a
-// piece) and per-row factors exchanged between lanes.
+constexpr int kM16VStride = 144;  // bf16 per V row in LDS (128 dims + pad: the transposing reads hit no bank twice)
+
+// One wave's LDS: the V tile, one row per token (also the output staging at
+// the end of a piece), and per-row factors exchanged between lanes.
 struct M16Lds {
-  uint16_t vt[kDim * kMfVtStride];
+  uint16_t vt[kTile * kM16VStride];
   float rowf[kM16Rows];
 };
 
@@ -86,20 +86,6 @@ __device__ __forceinline__ void m16_issue_k(const MfTile& tl, uint4 (&kr)[16]) {
   }
 }
 
-// The tile's V (loaded by mf_issue_v: vr[4 j + i] = chunk lane & 15 of token
-// 16 j + 4 (lane >> 4) + i) into LDS as it is: rows of kM16VStride bf16 per
-// token, one 16-byte store per chunk.
-constexpr int kM16VStride = 144;  // 128 dims + pad (288 B): the transposing reads hit no bank twice
-static_assert(kTile * kM16VStride <= kDim * kMfVtStride, "V rows fit the wave's LDS");
-__device__ __forceinline__ void m16_store_v(uint16_t* vt, const uint4 (&vr)[16]) {
-  const int lane = lane_id();
-  const int ch = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(vt + (16 * j + 4 * (lane >> 4) + i) * kM16VStride + 8 * ch) = vr[4 * j + i];
-}
 
 // Q^T of segment (b, g) as B operands: dims 32 ks + 8 j .. +7 of row l % 16;
 // padding rows are zero.  A negative scale's sign goes into q (exact in
@@ -273,7 +259,7 @@ __device__ int m16_stream_run(const DecodeArgs& a, const TileScan& sc, int pos, 
 
     // --- V of this tile into LDS, then V of tile i + 1 into its registers
     lds_order();
-    m16_store_v(L.vt, vr);
+    mf_store_v_rows<kM16VStride>(L.vt, vr);
     mf_issue_v(t1, vr);
     lds_order();
 
@@ -343,13 +329,8 @@ __device__ int m16_stream_run(const DecodeArgs& a, const TileScan& sc, int pos, 
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const int off0 = 32 * ks * kM16VStride + 16 * n;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0 + 16 * kM16VStride));
-        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[ks], __builtin_bit_cast(bf16x8_t, both), o[n], 0, 0, 0);
+        const bf16x8_t vop = tr_read_pair(vsrc + 32 * ks * kM16VStride + 16 * n, 16 * kM16VStride);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[ks], vop, o[n], 0, 0, 0);
       }
     lds_order();
 

@@ -358,6 +358,17 @@ def spec_verify_decode() -> PagedCase:
                      q_lens=np.full(64, 6, dtype=np.int64), rng=rng)
 
 
+def spec_verify_decode_g4() -> PagedCase:
+    """Speculative verification with 5 drafted tokens at 4 query heads per kv
+    head: the batch of spec_verify_decode (64 sequences, 6 new tokens each
+    over U{512..4096} cached tokens) with 32 q / 8 kv heads, so a (sequence,
+    kv head) holds 24 query rows."""
+    rng = np.random.default_rng(9)
+    ctx = rng.integers(512, 4096, size=64, endpoint=True)
+    return make_case("spec_verify_decode_g4", "prefill", 9, ctx, 32, 8,
+                     q_lens=np.full(64, 6, dtype=np.int64), rng=rng)
+
+
 def long_prefix_chunk() -> PagedCase:
     """One long prompt mid-way through chunked prefill: a 512-token chunk on
     top of a 65,536-token cached prefix, one sequence; 16 q / 8 kv heads."""
@@ -386,6 +397,7 @@ CONFIGS = {
     "multi_query_decode": multi_query_decode,
     "long_prefix_chunk": long_prefix_chunk,
     "spec_verify_decode": spec_verify_decode,
+    "spec_verify_decode_g4": spec_verify_decode_g4,
     "long_chunk_with_decode": long_chunk_with_decode,
 }
 
