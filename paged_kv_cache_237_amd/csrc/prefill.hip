@@ -10,6 +10,9 @@
 // One workgroup = 4 waves = 128 query rows (G heads x 128/G positions) of one
 // (sequence, kv head), so every K/V tile staged in LDS serves all G heads.
 // Tiles of 64 keys never straddle a 256-token block (one table lookup each).
+// A tile's K and V go straight from memory into LDS (buffer_load ... lds, no
+// registers on the way), two LDS buffers deep: tile t+1 is in flight while
+// tile t is computed.
 // Per wave and tile (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   S^T = K Q^T : A = K rows from LDS (16 B per lane, the cache's 8-dim chunks),
 //                 B = the wave's 32 query rows, held in registers for the whole
@@ -20,8 +23,9 @@
 //                 contraction runs over keys in the accumulator's register
 //                 order (per 16 keys, lane half h holds keys 4h..4h+3 and
 //                 8+4h..8+4h+3), so P never moves between lanes.  V is kept
-//                 in LDS as it is in the cache ([key][dim], one 16-byte store
-//                 per chunk), and a lane's B operand -- its dim of those 8
+//                 in LDS as it is in the cache ([key][dim], 256-byte rows
+//                 whose 16-byte chunks are XOR-rotated by 4 (key mod 4)), and
+//                 a lane's B operand -- its dim of those 8
 //                 keys -- is gathered by two transposing LDS reads
 //                 (ds_read_b64_tr_b16: in each 16-lane group, lane j points
 //                 at 4 dims of key j / 4 and receives dim j % 4 of the
@@ -61,18 +65,19 @@ typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerWG = kPrefillRows;  // query rows (head, position) per workgroup: 32 per wave
 constexpr int kKeys = 64;        // keys per K/V tile
-constexpr int kVStride = 160;    // bf16 per V row (one key) in LDS: 128 dims + pad, 320 B
+constexpr int kVStride = kDim;   // bf16 per V row (one key) in LDS
 constexpr float kLazyRescale = 8.f;  // log2 headroom before O is rescaled
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
 // LDS: two K tiles and two V tiles; tile t is read from buffer t&1 while
-// tile t+1 waits in registers.
+// tile t+1 is written into the other.  V row `key` holds dims 8 c .. 8 c + 7
+// in 16-byte chunk c ^ 4 (key & 3): the 4 keys that a 16-lane transposing
+// read spans then sit on 4 different quarters of the banks.
 struct __align__(16) PrefillLds {
   uint4 k[2][kChunks * kKeys];       // [buf][chunk][key] 16-byte chunks: 2 x 16 KiB
-  uint16_t v[2][kKeys * kVStride];   // [buf][key][dim] bf16: 2 x 20 KiB
+  uint16_t v[2][kKeys * kVStride];   // [buf][key][rotated chunk][8] bf16: 2 x 16 KiB
   float rowf[4][32];                 // per-wave row factors
 };
-constexpr size_t kPrefillLds = sizeof(PrefillLds);
 static_assert(sizeof(PrefillLds) >= 4 * 32 * kDim * 2, "epilogue staging fits");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -87,7 +92,9 @@ struct TileGeom {
 __device__ __forceinline__ TileGeom tile_geom(const PrefillArgs& a, const int32_t* table, int g,
                                               int ctx, int t) {
   const int key0 = t * kKeys;
-  const int phys = table[key0 / kBlock];
+  // a scalar load (the LDS-DMA writes would otherwise keep the compiler
+  // from proving the table unchanged, and it would use a vector load)
+  const int phys = ((const __attribute__((address_space(4))) int32_t*)table)[key0 / kBlock];
   const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
   TileGeom tg;
   tg.valid = ok ? min(kKeys, ctx - key0) : 0;
@@ -99,42 +106,32 @@ __device__ __forceinline__ TileGeom tile_geom(const PrefillArgs& a, const int32_
   return tg;
 }
 
-// K tile t -> registers: 4 chunks per thread.
-__device__ __forceinline__ void load_k(const PrefillArgs& a, const int32_t* table, int g, int ctx,
-                                       int t, int tid, uint4 (&kx)[4]) {
+// Tile t straight into the LDS buffers kbuf / vbuf.  In buffer_load ... lds,
+// lane l of an instruction writes its 16 bytes at the instruction's LDS base
+// + 16 l, and lanes outside the buffer's range write zeros (keys past the
+// context: the cache may hold NaN patterns there).  Wave w of 4 takes K
+// chunks w + 4 j (lane = key: 1 KiB of [chunk][key] per instruction) and V
+// rows 16 w + 4 i .. + 3 (16 lanes per 256-byte row, lane l reading the
+// chunk that belongs at position l % 16 of its rotated row).  The waves
+// wait for these with s_waitcnt vmcnt(0) and a barrier before reading.
+__device__ __forceinline__ void dma_tile(const PrefillArgs& a, const int32_t* table, int g, int ctx, int t,
+                                         int w, int lane, uint4* kbuf, uint16_t* vbuf) {
   const TileGeom tg = tile_geom(a, table, g, ctx, t);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = tid + 256 * j;
-    const int ch = i >> 6, row = i & 63;
-    const uint32_t off = row < tg.valid ? uint32_t(ch * kBlock + tg.r0 + row) * 16u : kOutOfRange;
-    kx[j] = buf_load16(tg.rk, off, 0u);
+    const int ch = w + 4 * j;
+    const uint32_t off = lane < tg.valid ? uint32_t(ch * kBlock + tg.r0 + lane) * 16u : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rk, (__attribute__((address_space(3))) void*)(kbuf + ch * kKeys),
+                                             16, off, 0, 0, 0);
   }
-}
-
-// V tile t -> registers: chunk tid & 15 of keys 4 (tid >> 4) .. +3, so that
-// 16 lanes read one key's whole 256-byte row.
-__device__ __forceinline__ void load_v(const PrefillArgs& a, const int32_t* table, int g, int ctx,
-                                       int t, int tid, uint4 (&vr)[4]) {
-  const TileGeom tg = tile_geom(a, table, g, ctx, t);
-  const int ch = tid & 15, kq = tid >> 4;
+  const int c = (lane & 15) ^ (4 * (lane >> 4));  // row 16 w + 4 i + l / 16 has key & 3 = l / 16
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    vr[i] = buf_load16(tg.rv, uint32_t((tg.r0 + 4 * kq + i) * kChunks + ch) * 16u, 0u);
-}
-
-__device__ __forceinline__ void store_k(uint4* kbuf, int tid, const uint4 (&kx)[4]) {
-  uint4* kdst = kbuf + tid;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) kdst[256 * j] = kx[j];
-}
-
-// V rows into LDS as they are ([key][dim], rows of kVStride): one 16-byte
-// store per chunk.
-__device__ __forceinline__ void store_v(uint16_t* vbuf, int tid, const uint4 (&vr)[4]) {
-  const int ch = tid & 15, kq = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(vbuf + (4 * kq + i) * kVStride + 8 * ch) = vr[i];
+  for (int i = 0; i < 4; ++i) {
+    const int row0 = 16 * w + 4 * i;
+    const uint32_t off = uint32_t((tg.r0 + row0 + (lane >> 4)) * kChunks + c) * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rv, (__attribute__((address_space(3))) void*)(vbuf + row0 * kVStride),
+                                             16, off, 0, 0, 0);
+  }
 }
 
 // Geometry of query block jrev (counted from the end) of sequence b, shared
@@ -394,8 +391,11 @@ __device__ void arrive_and_merge(const PrefillArgs& a, const BlockGeom<G>& bg, i
 constexpr int kShortRows = 16;
 constexpr int kSVStride = 144;  // bf16 per V row in a wave's LDS (128 dims + pad, 288 B)
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-static_assert(4 * kKeys * kSVStride * 2 + 4 * 16 * 4 <= sizeof(PrefillLds), "short-path LDS fits");
-static_assert(4 * (kShortRows * kDim + 2 * kShortRows) * 4 <= sizeof(PrefillLds), "short-path merge fits");
+// A workgroup's dynamic LDS: the main path's buffers or the short path's
+// four waves of V rows, whichever is larger.
+constexpr size_t kShortLds = 4 * kKeys * kSVStride * 2 + 4 * 16 * 4;
+constexpr size_t kPrefillLds = sizeof(PrefillLds) > kShortLds ? sizeof(PrefillLds) : kShortLds;
+static_assert(4 * (kShortRows * kDim + 2 * kShortRows) * 4 <= kPrefillLds, "short-path merge fits");
 
 // A 16-byte load with the non-temporal cache policy (NT bit of the buffer
 // builtins' cache-policy operand): the lines are not kept for reuse.
@@ -722,13 +722,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Tile t+1 is loaded into registers while tile t is computed from LDS;
-  // the two LDS buffers alternate.
-  uint4 kx[4], vr[4];
-  if (t_begin < t_end) {
-    load_k(a, table, g, ctx, t_begin, tid, kx);
-    load_v(a, table, g, ctx, t_begin, tid, vr);
-  }
+  // Tile t+1 is loaded into one LDS buffer while tile t is computed from
+  // the other.
+  if (t_begin < t_end) dma_tile(a, table, g, ctx, t_begin, w, lane, sm.k[t_begin & 1], sm.v[t_begin & 1]);
 
   const float c = fabsf(a.scale_log2);
   f32x16_t o[4];
@@ -739,9 +735,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY;  // running reference max of the lane's row (log2 units)
   float l = 0.f;        // partial row sum over this lane's keys
 
-  // S^T = K Q^T of tile t from K buffer t&1: two independent 32-key chains.
-  auto scores = [&](int t, f32x16_t (&s)[2]) {
-    const uint4* ksrc = sm.k[t & 1] + half * kKeys + col;  // chunk 2ks+half, key 32ms+col
+  // S^T = K Q^T of the tile in K buffer kb: two independent 32-key chains.
+  auto scores = [&](const uint4* __restrict__ kb, f32x16_t (&s)[2]) {
+    const uint4* ksrc = kb + half * kKeys + col;  // chunk 2ks+half, key 32ms+col
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
@@ -770,8 +766,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // Softmax of tile t's scores and O += P V with V buffer t&1.
-  auto softmax_pv = [&](int t, f32x16_t (&s)[2]) {
+  // Softmax of tile t's scores and O += P V with the tile in V buffer vb.
+  auto softmax_pv = [&](int t, const uint16_t* __restrict__ vb, f32x16_t (&s)[2]) {
     const int key0 = t * kKeys;
     // mask keys past the row's position (diagonal / tail tiles)
     if (key0 + kKeys - 1 > amin) {
@@ -836,12 +832,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // 16 ks + 4 half + {0..3} and 16 ks + 8 + 4 half + {0..3} (P's order),
     // two transposing LDS reads: in each 16-lane group, lane j points at dims
     // 4 (j & 3) .. +3 of key j >> 2 and receives its own dim of all 4 keys.
-    const uint16_t* vsrc = sm.v[t & 1] + (4 * half + (jl >> 2)) * kVStride + 16 * dg + 4 * (jl & 3);
+    // Those keys have key & 3 = j >> 2, so dims 32 n .. 32 n + 31 of the
+    // lane's row sit 32 (n ^ (j >> 2)) bf16 into it.
+    const uint16_t* vrow = vb + (4 * half + (jl >> 2)) * kVStride + 16 * dg + 4 * (jl & 3);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int off0 = 16 * ks * kVStride + 32 * n;  // bf16, compile-time
+        const uint16_t* vsrc = vrow + 32 * (n ^ (jl >> 2));
+        const int off0 = 16 * ks * kVStride;  // bf16, compile-time
         const int off1 = off0 + 8 * kVStride;
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
@@ -854,20 +853,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  for (int t = t_begin; t < t_end; ++t) {
-    // Buffer t&1 last held tile t-2, which every wave finished computing
-    // before the previous barrier.
-    store_k(sm.k[t & 1], tid, kx);
-    store_v(sm.v[t & 1], tid, vr);
-    if (t + 1 < t_end) {
-      load_k(a, table, g, ctx, t + 1, tid, kx);
-      load_v(a, table, g, ctx, t + 1, tid, vr);
-    }
-    __syncthreads();
-    if (t * kKeys > amax) continue;  // every key of the tile is above this wave's diagonal
+  // One tile: the loads of tile t+1 into buffers (kn, vn), then tile t from
+  // (kc, vc).  The restrict pointers tell the compiler that the LDS-DMA
+  // writes and this tile's LDS reads are disjoint; otherwise it would make
+  // every read wait for the writes just issued (the wait for a tile's own
+  // loads is the explicit one at the top of the loop).
+  auto step = [&](int t, const uint4* __restrict__ kc, const uint16_t* __restrict__ vc, uint4* __restrict__ kn,
+                  uint16_t* __restrict__ vn) {
+    if (t + 1 < t_end) dma_tile(a, table, g, ctx, t + 1, w, lane, kn, vn);
+    if (t * kKeys > amax) return;  // every key of the tile is above this wave's diagonal
     f32x16_t s[2];
-    scores(t, s);
-    softmax_pv(t, s);
+    scores(kc, s);
+    softmax_pv(t, vc, s);
+  };
+  for (int t = t_begin; t < t_end; ++t) {
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's part of tile t is in LDS
+    // every wave's part; and every wave is past tile t-1, whose buffers the
+    // loads of tile t+1 now overwrite
+    __syncthreads();
+    step(t, sm.k[t & 1], sm.v[t & 1], sm.k[(t + 1) & 1], sm.v[(t + 1) & 1]);
   }
 
   const float ltot = xor32_sum(l);
