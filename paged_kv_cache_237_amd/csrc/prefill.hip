@@ -932,8 +932,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 //   hkv: the records the host sizes for 2 slots x kRowsPerWG rows suffice.
 //   The parts merge without a second kernel (arrive_and_merge); the plan
 //   zeroes their arrival counters (plan_cnt, one per first slot and kv head).
-// * the order: the items (query block, part) counted per length (tiles of
-//   the part; kPlanBuckets - 1 and more counted together), the counts turned
+// * the order: the items (query block, part) counted per length (the whole
+//   block's tiles, 5/4 of them for a short block; kPlanBuckets - 1 and more
+//   counted together), the counts turned
 //   into offsets in order of decreasing length, every item written at its
 //   offset; items of one length keep no particular order and record slots
 //   go to cut blocks in no particular order (each item writes its own rows
@@ -998,9 +999,14 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
         for (int g = 0; g < a.hkv; ++g) a.plan_cnt[slot * a.hkv + g] = 0;  // arrival counters
       }
       // the parts of a cut block go by the whole block's length, so that
-      // they start in the first round rather than after every longer item
+      // they start in the first round rather than after every longer item;
+      // a short block (the short-row path: memory-bound, so its tiles take
+      // longer than a chunk's while the chip streams) counts 5/4 of its
+      // tiles (chunked prefill mixed with decode rows 252.6 -> 245.8 us,
+      // 248.3 -> 241.4 us; 4/3, 3/2 and 2 gained less, 2/3 lost)
+      const int len = bg.qlen * G <= kShortRows ? bg.ntiles * 5 / 4 : bg.ntiles;
       for (int part = 0; part < bg.nsplit; ++part)
-        fn(int(c) * 16 + part, kPlanBuckets - 1 - min(bg.ntiles, kPlanBuckets - 1));
+        fn(int(c) * 16 + part, kPlanBuckets - 1 - min(len, kPlanBuckets - 1));
     }
   };
   for_items(true, [&](int, int key) { atomicAdd(&cnt[key], 1); });
