@@ -99,6 +99,12 @@ def test_speculative_verification_workload():
     check(wl.spec_verify_decode(), 6)
 
 
+def test_speculative_verification_four_heads_per_kv_head():
+    """The same batch at 32 q / 8 kv heads: 24 rows per (sequence, kv head),
+    the 32-row matrix-core kernel, at the size the benchmark times."""
+    check(wl.spec_verify_decode_g4(), 6)
+
+
 @pytest.mark.parametrize("hq", [16, 32])
 def test_decode_multi_many_rows_matches_prefill(hq):
     """The same rows through pa_prefill (a varlen batch with q_len = 6 and a

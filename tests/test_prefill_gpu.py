@@ -103,6 +103,13 @@ def test_multi_query_decode():
     check(wl.multi_query_decode())
 
 
+def test_speculative_verification_workload():
+    """5 drafted tokens plus the next one per sequence (64 x 6 rows over
+    U{512..4096} cached tokens, 12 rows per kv head: the short-row path), at
+    the size the benchmark times through pa_prefill."""
+    check(wl.spec_verify_decode())
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8)])
 def test_prefill_long_prefix_split_many_ways(hq, hkv):
     """Query blocks over cached prefixes of up to 20,000 keys: their key
