@@ -191,16 +191,14 @@ def _events_batch_ms(fn, steps):
     return a.elapsed_time(b) / steps
 
 
-def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True) -> dict:
+def time_decode(case: wl.PagedCase, steps: int, warmup: int) -> dict:
     """Times `steps` decode steps after `warmup`.  A step stores each
     sequence's new token and attends over the whole context; it runs as one
     pa_decode_append launch ("step_ms", the headline) and, for comparison, as
     pa_store_kv + pa_decode ("two_call_step_ms").  Whole steps are launched
     back to back on one stream (the host stays far ahead of a step of this
-    size, so the GPU sees no launch gaps) and, beside that, captured once in
-    a HIP graph and replayed ("*_graph_ms"; each replay of a graph this small
-    adds a few microseconds of its own).  graph=False skips the graph
-    timings.  Kernel
+    size, so the GPU sees no launch gaps); their HIP-graph replays are timed
+    apart (time_decode_graphs), after every single-stream measurement.  Kernel
     times ("append_ms", "decode_ms", "store_ms") are HIP events around
     `steps` eager calls launched back to back on the stream the kernels run
     on, divided by `steps`; "decode_ms_flushed" are
@@ -255,12 +253,51 @@ def time_decode(case: wl.PagedCase, steps: int, warmup: int, graph: bool = True)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
-    if graph:
-        res["two_call_step_graph_ms"] = whole(_graph_of(two_calls).replay)
-        res["step_graph_ms"] = whole(_graph_of(append).replay)
     res["two_call_step_ms"] = whole(two_calls)
     res["step_ms"] = whole(append)
     del dev
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_decode_graphs(case: wl.PagedCase, steps: int, warmup: int) -> dict:
+    """The steps of time_decode captured once each in a HIP graph and replayed
+    back to back ("step_graph_ms", "two_call_step_graph_ms"; a replay of a
+    graph this small adds a few microseconds of its own).  The capture runs
+    on a stream of its own, and once a process has launched work on a second
+    stream, later launches on the default stream run slower (measured: an
+    8 x 128K decode step 636 -> 653 us per launch after one call on another
+    stream, back to ~636 us once the graph is freed), so main() times the
+    graphs, and the two-stream forms of the mixed batch, after everything
+    else."""
+    dev = place(case)
+    k_new, v_new = new_rows(dev)
+    out = torch.empty((case.batch, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    ws = pa.alloc_decode_workspace(case.batch, case.num_q_heads, case.num_kv_heads)
+
+    def append():
+        pa.decode_append(out, dev.q, k_new, v_new, dev.k_cache, dev.v_cache, dev.block_table,
+                         dev.context_lens, case.max_context_len, case.scale, ws)
+
+    def two_calls():
+        pa.store_kv(dev.step_k, dev.step_v, dev.step_slots, dev.k_cache, dev.v_cache)
+        pa.decode(out, dev.q, dev.k_cache, dev.v_cache, dev.block_table, dev.context_lens,
+                  case.max_context_len, case.scale, ws)
+
+    def whole(run):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    g2, g1 = _graph_of(two_calls), _graph_of(append)
+    res = {"two_call_step_graph_ms": whole(g2.replay), "step_graph_ms": whole(g1.replay)}
+    del g1, g2, dev
     torch.cuda.empty_cache()
     return res
 
@@ -1085,7 +1122,7 @@ def main(argv=None):
         return 2
     print(f"[bench] {case.name}: B={case.batch} sum_ctx={int(case.context_lens.sum())}",
           file=sys.stderr, flush=True)
-    t = time_decode(case, args.steps, args.warmup, graph=not args.no_graph)
+    t = time_decode(case, args.steps, args.warmup)
     copy_probe(args.copy_probe_mib)
     ceiling = read_ceiling([append_bytes(case), 4 << 30], ["step_bytes", "4GiB"])
     head = decode_entry(case, t, cus, ceiling)
@@ -1130,8 +1167,6 @@ def main(argv=None):
                      "long_prefix_chunk", "long_chunk_with_decode"):
             print(f"[bench] extra {name}", file=sys.stderr, flush=True)
             extra[name] = varlen_report(name, max(30, args.steps // 5), 3)
-        print("[bench] extra chunked_prefill_mixed split by kernel", file=sys.stderr, flush=True)
-        extra["chunked_prefill_mixed_split"] = mixed_split_report(max(30, args.steps // 5), 3)
         for name in ("multi_query_decode", "spec_verify_decode", "spec_verify_decode_g4"):
             print(f"[bench] extra {name} (pa_decode_multi)", file=sys.stderr, flush=True)
             extra[f"{name}_multi"] = decode_multi_report(name, max(20, args.steps // 5), 3)
@@ -1140,6 +1175,19 @@ def main(argv=None):
         print("[bench] extra block manager (host)", file=sys.stderr, flush=True)
         extra["block_manager"] = block_manager_report()
         line["extra"] = extra
+    # last: what launches work on a second stream (see time_decode_graphs)
+    if not args.no_graph:
+        print("[bench] graph replays", file=sys.stderr, flush=True)
+        entries = [(case, line)] + [(wl.CONFIGS[n](), line["extra"][n]) for n in DECODE_WORKLOADS
+                                    if not args.no_extra and n in line["extra"]]
+        for c, e in entries:
+            tg = time_decode_graphs(c, args.steps if c is case else max(10, args.steps // 5),
+                                    args.warmup if c is case else 3)
+            e["step_graph_replay_ms"] = round(tg["step_graph_ms"], 4)
+            e["two_call_step"]["graph_replay_ms"] = round(tg["two_call_step_graph_ms"], 4)
+    if not args.no_extra:
+        print("[bench] extra chunked_prefill_mixed split by kernel", file=sys.stderr, flush=True)
+        line["extra"]["chunked_prefill_mixed_split"] = mixed_split_report(max(30, args.steps // 5), 3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case, max_seqs=2 if case.max_context_len > 65536 else 0)
