@@ -264,12 +264,11 @@ def time_decode_graphs(case: wl.PagedCase, steps: int, warmup: int) -> dict:
     """The steps of time_decode captured once each in a HIP graph and replayed
     back to back ("step_graph_ms", "two_call_step_graph_ms"; a replay of a
     graph this small adds a few microseconds of its own).  The capture runs
-    on a stream of its own, and once a process has launched work on a second
-    stream, later launches on the default stream run slower (measured: an
-    8 x 128K decode step 636 -> 653 us per launch after one call on another
-    stream, back to ~636 us once the graph is freed), so main() times the
-    graphs, and the two-stream forms of the mixed batch, after everything
-    else."""
+    on a stream of its own, and after a process moves its work between
+    streams the kernels that follow can run ~3 % slower (an 8 x 128K decode
+    step 636-641 -> 653-660 us per launch, not after every switch), so
+    main() times the graphs, and the two-stream forms of the mixed batch,
+    after everything else."""
     dev = place(case)
     k_new, v_new = new_rows(dev)
     out = torch.empty((case.batch, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
