@@ -548,21 +548,29 @@ __device__ void prefill_short(const PrefillArgs& a, const BlockGeom<G>& bg, int 
     }
     // O += P V: lane (dim 16 nb + col, group grp) gathers keys 32 ks + 16 r +
     // 4 grp + {0..3} with transposing reads (lane col points at dims 4 (col &
-    // 3) .. +3 of key 32 ks + 16 r + 4 grp + col / 4)
+    // 3) .. +3 of key 32 ks + 16 r + 4 grp + col / 4).  MFMA i = 8 ks + nb;
+    // its operand is read kVAhead MFMAs ahead, in this fixed order (left to
+    // itself, the compiler puts every operand in one register quad and waits
+    // for each read right before its MFMA).
     const uint16_t* vsrc = vbuf + (4 * grp + (col >> 2)) * kSVStride + 4 * (col & 3);
+    auto vop_of = [&](int i) {
+      const int off0 = 32 * (i >> 3) * kSVStride + 16 * (i & 7);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0 + 16 * kSVStride));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int kVAhead = 4;
+    bf16x8_t vop[16];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int i = 0; i < kVAhead; ++i) vop[i] = vop_of(i);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int off0 = 32 * ks * kSVStride + 16 * nb;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0 + 16 * kSVStride));
-        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[ks], __builtin_bit_cast(bf16x8_t, both), o[nb], 0, 0,
-                                                        0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + kVAhead < 16) vop[i + kVAhead] = vop_of(i + kVAhead);
+      o[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop[i >> 3], vop[i], o[i & 7], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_wave_barrier();
   }
   const float ltot = xor32_sum(xor16_sum(l));
@@ -769,6 +777,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // Softmax of tile t's scores and O += P V with the tile in V buffer vb.
   auto softmax_pv = [&](int t, const uint16_t* __restrict__ vb, f32x16_t (&s)[2]) {
     const int key0 = t * kKeys;
+    // V operand (k-step ks, dims 32 n + col) of the product below
+    const uint16_t* vrow = vb + (4 * half + (jl >> 2)) * kVStride + 16 * dg + 4 * (jl & 3);
+    auto vop_of = [&](int ks, int n) {
+      const uint16_t* vsrc = vrow + 32 * (n ^ (jl >> 2)) + 16 * ks * kVStride;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(vsrc));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(vsrc + 8 * kVStride));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // the first k-step's operands are read now, while the score MFMAs finish,
+    // rather than right before the first product MFMA
+    bf16x8_t v0[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) v0[n] = vop_of(0, n);
+    __builtin_amdgcn_sched_barrier(0);
     // mask keys past the row's position (diagonal / tail tiles)
     if (key0 + kKeys - 1 > amin) {
 #pragma unroll
@@ -834,23 +857,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // 4 (j & 3) .. +3 of key j >> 2 and receives its own dim of all 4 keys.
     // Those keys have key & 3 = j >> 2, so dims 32 n .. 32 n + 31 of the
     // lane's row sit 32 (n ^ (j >> 2)) bf16 into it.
-    const uint16_t* vrow = vb + (4 * half + (jl >> 2)) * kVStride + 16 * dg + 4 * (jl & 3);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint16_t* vsrc = vrow + 32 * (n ^ (jl >> 2));
-        const int off0 = 16 * ks * kVStride;  // bf16, compile-time
-        const int off1 = off0 + 8 * kVStride;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off0));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(vsrc + off1));
-        const v8i16_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, both);
-        o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], vop, o[n], 0, 0, 0);
-      }
-    }
+      for (int n = 0; n < 4; ++n)
+        o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[ks], ks == 0 ? v0[n] : vop_of(ks, n), o[n], 0, 0, 0);
   };
 
   // One tile: the loads of tile t+1 into buffers (kn, vn), then tile t from
