@@ -170,13 +170,11 @@ __device__ void mf_merge(const DecodeArgs& a, int seg, int b, int g, int w0, int
   }
 }
 
-// Streams tiles [pos, end) of the flattened list (this wave's run) with two
-// tiles in flight: the K and V of tile i + 1 arrive in one register buffer
-// while tile i is computed from the other, and the loads of tile i + 2 go
-// into tile i's buffer as soon as its K has been used (after the scores)
-// and its V is in LDS -- also across segment boundaries (block-table entries
-// are fetched two tiles ahead; the next segment's q is loaded when a piece
-// ends).  Each piece (run ∩
+// Streams tiles [pos, end) of the flattened list (this wave's run) with
+// kMfDepth tiles in flight: the loads of tile i + kMfDepth go into the
+// registers tile i frees (K after its scores, V after its store to LDS) --
+// also across segment boundaries (block-table entries are looked up ahead;
+// the next segment's q is loaded when a piece ends).  Each piece (run ∩
 // segment) ends with either the bf16 output (whole segment) or a partial
 // record at seg + wave.  Returns the number of cut segments, whose (b, g,
 // first run, last run) go to pend_*.
