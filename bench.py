@@ -301,6 +301,17 @@ def time_decode_graphs(case: wl.PagedCase, steps: int, warmup: int) -> dict:
     return res
 
 
+def prefill_bytes(case: wl.PagedCase) -> int:
+    """Algorithmic bytes of one pa_prefill: q in and out written, every
+    cached K and V row of every context once, block-table entries used,
+    lengths and query offsets."""
+    rows = int(case.q_lens.sum())
+    sum_ctx = int(case.context_lens.sum())
+    d, hkv, hq, b = case.head_dim, case.num_kv_heads, case.num_q_heads, case.batch
+    blocks = sum(wl.blocks_for(int(n)) for n in case.context_lens)
+    return 2 * rows * hq * d * 2 + sum_ctx * hkv * d * 2 * 2 + 4 * blocks + 4 * b + 4 * (b + 1)
+
+
 def prefill_flops(case: wl.PagedCase) -> int:
     """Causal FLOPs of one pa_prefill: 4*D per (query row, visible key) pair
     per query head (q.k and p.v, a multiply and an add each)."""
@@ -359,6 +370,7 @@ def prefill_report(steps: int, warmup: int) -> dict:
     sto, pre = time_prefill(c, steps, warmup)
     fl = prefill_flops(c)
     sb = store_bytes(c.total_kv_rows, c.num_kv_heads)
+    pb = prefill_bytes(c)
     tf = fl / (pre * 1e-3) / 1e12
     return {"workload": c.name, "prefill_ms": round(pre, 4), **PREFILL_SPREAD.get(c.name, {}),
             "causal_gflop": round(fl / 1e9, 3),
@@ -373,7 +385,8 @@ def prefill_report(steps: int, warmup: int) -> dict:
             "prefill_roofline": {"bound": "mfma", "kernel": "prefill_kernel<2>",
                                  "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                 "traffic": None, "algorithmic_flops_per_launch": fl},
+                                 "traffic": recorded_prefill_traffic(), "algorithmic_flops_per_launch": fl,
+                                 "algorithmic_bytes_per_launch": pb},
             "store_roofline": {"bound": "hbm", "kernel": "store_kv_kernel",
                                "achieved": round(sb / (sto * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                                "unit": "GB/s",
@@ -832,6 +845,20 @@ def recorded_store_traffic():
     return int(round(rec["traffic_bytes"]))
 
 
+PREFILL_TRAFFIC = os.path.join(PROFILES, "prefill_8x2048_traffic.json")
+
+
+def recorded_prefill_traffic():
+    """HBM bytes per launch of the 8 x 2048 prefill from the committed
+    counter summary, if the prefill sources have not changed since."""
+    if not os.path.exists(PREFILL_TRAFFIC):
+        return None
+    rec = json.load(open(PREFILL_TRAFFIC))
+    if rec.get("source_sha256_16") != prefill_digest():
+        return None
+    return int(round(rec["traffic_bytes"]))
+
+
 def recorded_traffic(workload: str):
     """Traffic per launch from the committed counter summary of this workload,
     if the decode kernel source has not changed since it was taken."""
@@ -1071,7 +1098,7 @@ def main(argv=None):
     ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
                     help="OUT_MD KERNEL_KEY CSV [CSV ...]: write a summary of SQ/GRBM counter "
                          "CSVs of one kernel (rocprofv3 --pmc passes) and exit")
-    ap.add_argument("--traffic-source", choices=("decode", "store"), default="decode",
+    ap.add_argument("--traffic-source", choices=("decode", "store", "prefill"), default="decode",
                     help="kernel whose source digest a traffic summary records (default: decode)")
     ap.add_argument("--commands", nargs="*", default=[],
                     help="the profiler commands recorded in a traffic summary")
@@ -1081,7 +1108,7 @@ def main(argv=None):
         return 0
     if args.summarize_traffic:
         f, w, mib, key, out = args.summarize_traffic
-        src = DECODE_SRC if args.traffic_source == "decode" else STORE_SRC
+        src = {"decode": DECODE_SRC, "store": STORE_SRC, "prefill": PREFILL_SRC}[args.traffic_source]
         print(json.dumps(summarize_traffic(f, w, int(mib), key, out, args.commands, src)))
         return 0
     if args.summarize_counters:

@@ -33,6 +33,28 @@ def test_prefill_flops_count_visible_pairs_only():
     assert bench.prefill_flops(c) == 4 * 128 * 16 * pairs
 
 
+def test_prefill_bytes_count_q_out_and_each_context_once():
+    # q rows in and out (every head), K and V rows of every context once,
+    # table entries of the contexts, lengths and the query offsets
+    c = wl.make_case("pb", "prefill", 3, [5, 300], 16, 8, q_lens=[5, 3])
+    want = 2 * (5 + 3) * 16 * 128 * 2 + (5 + 300) * 8 * 128 * 2 * 2 + 4 * (1 + 2) + 4 * 2 + 4 * 3
+    assert bench.prefill_bytes(c) == want
+
+
+def test_committed_prefill_traffic_summary_is_current_and_plausible():
+    """The prefill traffic summary records the current prefill sources; its
+    writes are the output rows exactly (each written once) and its reads lie
+    between the algorithmic reads (q, every K/V row once) and a few times
+    them (K/V rows re-fetched after L2 eviction)."""
+    rec = json.load(open(os.path.join(ROOT, "profiles", "prefill_8x2048_traffic.json")))
+    assert rec["source_sha256_16"] == bench.prefill_digest()
+    c = wl.prefill_8x2048()
+    out_bytes = int(c.q_lens.sum()) * c.num_q_heads * c.head_dim * 2
+    assert abs(rec["write_bytes"] - out_bytes) <= 0.01 * out_bytes
+    reads = bench.prefill_bytes(c) - out_bytes
+    assert reads <= rec["fetch_bytes"] < 4 * reads
+
+
 def _write_counter_csv(path, rows):
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
