@@ -333,7 +333,10 @@ def test_brute_force_tiny(bs):
         d = 8 * int(rng.integers(1, 3))
         lens = [int(x) for x in rng.integers(1, 10, size=3)]
         kind = "prefill" if trial % 2 else "decode"
-        case = small_case(100 * bs + trial, lens, hq, hkv, d=d, bs=bs, kind=kind,
+        # prefill rows: the last q_len of each context, q_len in 1..ctx (a
+        # cached prefix of ctx - q_len tokens where q_len < ctx)
+        q_lens = [int(rng.integers(1, n + 1)) for n in lens] if kind == "prefill" else None
+        case = small_case(100 * bs + trial, lens, hq, hkv, d=d, bs=bs, kind=kind, q_lens=q_lens,
                           q_mult=float(2 ** int(rng.integers(0, 5))))
         q, k, v = case_tensors(case)
         kp, vp = build_pools(case, k, v)
